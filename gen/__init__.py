@@ -43,6 +43,7 @@ import numpy as np
 
 __all__ = [
     "CONFIGS",
+    "custom_spec",
     "Workload",
     "make_workload",
     "make_weights",
@@ -85,6 +86,17 @@ CONFIGS = {
 # FFN buffer of 8 x 120 rows.
 C4_WORKER_ROWS = 120
 C4_WORKER_COUNTS = (120, 1, 1, 1, 1, 1, 1, 1)
+
+
+def custom_spec(name: str, T: int, K: int, E: int, G: int, H: int, I: int, dtype: str = "bf16",
+                routing: str = "zipf", zipf_s: float = 1.0, need_local: bool = True,
+                seed: int = 1) -> ConfigSpec:
+    """A workload spec outside the five named ones (reduced sizes for checks
+    that the CPU oracle must finish in seconds). Registered under `name`."""
+    spec = ConfigSpec(name, T=T, K=K, E=E, G=G, H=H, I=I, dtype=dtype, routing=routing,
+                      zipf_s=zipf_s, need_local=need_local, seed=seed)
+    CONFIGS[name] = spec
+    return spec
 
 
 @dataclasses.dataclass

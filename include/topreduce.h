@@ -1,0 +1,165 @@
+/*
+ * topreduce.h -- C ABI of libtopreduce.so: one GPU's share of an
+ * expert-parallel MoE FFN on MI355X (gfx950).
+ *
+ * The problem (DeepEP issue #48, "How to apply MoE MLP to recv_x returned by
+ * dispatch when num_expert_per_rank > 1", question and answers): after
+ * dispatch a rank holds each received token once, as a row of recv_x, with its
+ * top-k expert ids and gate weights. To run the local experts as a grouped
+ * GEMM every token is expanded once per local expert it is routed to; after
+ * the experts, a reduction folds each token's expert outputs back into one row
+ * so that the result keeps recv_x's row count and order, which combine's
+ * dispatch handle requires. DeepEP issue #760 ("DeepEP V2 combine epilogue low
+ * batch performance") shows this weighted reduce as the combine epilogue and
+ * its low-batch straggling when one warp serves one token.
+ *
+ * The path, per call sequence:
+ *   moe_plan     route scan: per-expert counts and segment offsets, and the
+ *                stable maps between received slots and expanded rows
+ *   moe_forward  = moe_expand + moe_grouped_gemm + moe_combine_reduce
+ *
+ * Conventions for every entry point:
+ *  - Pointers named "device" are HIP device (or managed) memory; the others
+ *    are host memory. The caller allocates and owns every buffer, including
+ *    the workspace; the library allocates nothing and keeps no per-call state.
+ *  - All work is enqueued on `stream` (NULL: the null stream) and returns
+ *    without synchronising, except moe_plan_stats, which waits on `stream`.
+ *    Calls are graph-capturable except moe_plan_stats.
+ *  - Arrays are dense and row-major. x, y, W1, W2 and the expert buffers are
+ *    all of one element type, desc->dtype.
+ *  - Errors: a non-zero tr_status and a message in moe_last_error(). Argument
+ *    checks happen on the host before anything is enqueued. Nothing aborts.
+ *  - Ids outside [expert_begin, expert_begin + E), -1 included, are routes to
+ *    other ranks or padding: they are ignored, never an error, and their
+ *    weights are never read (DeepEP issue #760, repro script: routes below 0
+ *    are masked out before the local weight sum).
+ */
+#ifndef TOPREDUCE_H
+#define TOPREDUCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TR_ABI_VERSION 1
+
+typedef enum {
+    TR_OK = 0,
+    TR_EINVAL = -1,        /* bad argument: null/misaligned pointer, bad size */
+    TR_EUNSUPPORTED = -2,  /* valid but not supported shape or dtype */
+    TR_EWORKSPACE = -3,    /* workspace smaller than moe_workspace_size() */
+    TR_EHIP = -4           /* a HIP runtime call failed */
+} tr_status;
+
+typedef enum { TR_BF16 = 0, TR_F32 = 1 } tr_dtype;
+typedef enum { TR_IDX_I32 = 0, TR_IDX_I64 = 1 } tr_idx_dtype;
+
+/* Grouped-GEMM kernel choice. AUTO sends experts with at most 32 routes to the
+ * weight-streaming kernel and the others to the tiled MFMA kernel; the FORCE
+ * flags send every expert to one of them (for testing). */
+#define TR_FLAG_GEMM_FORCE_TILED 0x1
+#define TR_FLAG_GEMM_FORCE_STREAM 0x2
+
+typedef struct tr_moe_desc {
+    int64_t T;             /* received rows (recv_x rows), >= 0 */
+    int32_t K;             /* top-k slots per row, 1..32 */
+    int32_t E;             /* local experts, 1..1024 */
+    int64_t expert_begin;  /* global id of local expert 0 */
+    int64_t H;             /* hidden size */
+    int64_t I;             /* SwiGLU intermediate size */
+    int32_t dtype;         /* tr_dtype of x, y, W1, W2 */
+    int32_t idx_dtype;     /* tr_idx_dtype of topk_idx */
+    int32_t flags;         /* TR_FLAG_* */
+    int32_t reserved;
+} tr_moe_desc;
+
+/* Host-side handle returned by moe_plan: the descriptor plus device pointers
+ * into the caller's workspace. Valid while that workspace lives and until the
+ * next moe_plan on the same workspace; reusable for any number of forwards.
+ * Row-index arrays are int32. */
+typedef struct tr_moe_plan {
+    tr_moe_desc d;
+    int64_t R_cap;         /* T * K: upper bound of expanded rows */
+    void* ws;
+    size_t ws_bytes;
+    int32_t* counts;       /* [E] routes per local expert */
+    int32_t* offsets;      /* [E+1] segment starts; offsets[E] = R */
+    int32_t* row_map;      /* [T*K] expanded row of slot (t,k), or -1 */
+    int32_t* row_src;      /* [R_cap] received row of expanded row r (r < R) */
+    int32_t* row_k;        /* [R_cap] slot of expanded row r (r < R) */
+    int32_t* stats;        /* [4] R, rows with >= 1 local route, ignored slots, empty experts */
+    int32_t* scan_tmp;     /* route-scan block partials */
+    void* Xe;              /* [R_cap, H] expanded rows (expert-contiguous) */
+    void* h;               /* [R_cap, I] silu(gate) * up */
+    void* O;               /* [R_cap, H] expert outputs */
+    int32_t scan_blocks;
+    int32_t scan_rows_per_block;
+} tr_moe_plan;
+
+/* Bytes of device workspace a plan for `desc` needs (every buffer above,
+ * 256-byte aligned). Returns 0 and sets the last error if desc is invalid. */
+size_t moe_workspace_size(const tr_moe_desc* desc);
+
+/* Route scan (DeepEP issue #48 answer: expand each token to its experts before
+ * the grouped GEMM). topk_idx: device [T, K] of idx_dtype, global expert ids
+ * or -1. ws: device, ws_bytes >= moe_workspace_size(desc), 256-byte aligned.
+ * Fills *out (host) and enqueues the scan: counts, offsets, row_map, row_src,
+ * row_k and stats are written on the device. Row order: an expert's segment
+ * lists its routes by received row, then by slot. Bit-exact and deterministic.
+ * topk_idx may be freed once the stream has passed this call. */
+tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size_t ws_bytes,
+                   hipStream_t stream, tr_moe_plan* out);
+
+/* Whole layer: y[t] = sum over local slots k (ascending) of
+ * topk_weights[t][k] * MLP_e(x[t]), with MLP_e(x) = W2[e] (silu(W1[e][0:I] x) *
+ * (W1[e][I:2I] x)). Rows without a local slot are written as +0.
+ * x: device [T, H]; topk_weights: device fp32 [T, K] or NULL for weight 1
+ * (combine called without weights in DeepEP issue #760's repro);
+ * w1: device [E, 2I, H] (rows [0, I) gate, [I, 2I) up); w2: device [E, H, I];
+ * y: device [T, H], may alias x; no other aliasing. Accumulation is fp32;
+ * for bf16 the intermediate h and expert outputs are rounded to bf16.
+ * Equivalent to moe_expand, moe_grouped_gemm, moe_combine_reduce(plan, NULL,
+ * topk_weights, y). */
+tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_weights,
+                      const void* w1, const void* w2, void* y, hipStream_t stream);
+
+/* Expand (DeepEP issue #48 answer): Xe[r] = x[row_src[r]] for r < R, a bit
+ * copy into the plan's expert-contiguous buffer. x: device [T, H]. */
+tr_status moe_expand(const tr_moe_plan* plan, const void* x, hipStream_t stream);
+
+/* Grouped SwiGLU GEMM over the plan's Xe: h = silu(Xe W1g^T) * (Xe W1u^T) per
+ * expert segment, then O = h W2^T. Empty experts and rows past each segment
+ * cost no MFMA work (SGLang PR #6092: padded rows must not add computation). */
+tr_status moe_grouped_gemm(const tr_moe_plan* plan, const void* w1, const void* w2,
+                           hipStream_t stream);
+
+/* Weighted top-k reduce (DeepEP issue #48: the reduction before the combine
+ * all-to-all; DeepEP issue #760: the combine epilogue, one row per received
+ * token): y[t] = sum over k ascending with row_map[t][k] >= 0 of
+ * topk_weights[t][k] * expert_out[row_map[t][k]], accumulated in fp32.
+ * expert_out: device [>= R, H] of dtype, or NULL for the plan's O.
+ * topk_weights: device fp32 [T, K] or NULL (weight 1). y: device [T, H].
+ * The hidden dimension is split across wavefronts so that a few tokens still
+ * occupy many compute units. */
+tr_status moe_combine_reduce(const tr_moe_plan* plan, const void* expert_out,
+                             const float* topk_weights, void* y, hipStream_t stream);
+
+/* Copies stats to host_out[4] = {R, rows with a local route, ignored slots,
+ * empty experts} and synchronises `stream` (opt-in host sync, the counterpart
+ * of dispatch's do_cpu_sync in DeepEP issue #760's repro). */
+tr_status moe_plan_stats(const tr_moe_plan* plan, int32_t* host_out, hipStream_t stream);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+/* TR_ABI_VERSION of the built library. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,132 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry
+point the header declares, its structs match the binding's mirror, and host
+argument checks return the documented status codes before touching a GPU."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import top_reduce_amd as tr
+from top_reduce_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "topreduce.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(moe_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for n in ("moe_workspace_size", "moe_plan", "moe_forward", "moe_expand", "moe_grouped_gemm",
+              "moe_combine_reduce", "moe_plan_stats", "moe_last_error", "moe_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tr.load_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", tr.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)", out))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert lib.moe_abi_version() == B.ABI_VERSION
+
+
+def test_struct_layout_matches_binding(tmp_path):
+    prog = tmp_path / "layout.c"
+    fields_d = [f for f, _ in B.Desc._fields_]
+    fields_p = [f for f, _ in B.PlanStruct._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "topreduce.h"', "int main(void){",
+             'printf("%zu %zu\\n", sizeof(tr_moe_desc), sizeof(tr_moe_plan));']
+    lines += [f'printf("%zu\\n", offsetof(tr_moe_desc, {f}));' for f in fields_d]
+    lines += [f'printf("%zu\\n", offsetof(tr_moe_plan, {f}));' for f in fields_p]
+    lines += ["return 0;}"]
+    prog.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(prog), "-o", str(exe)], check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == C.sizeof(B.Desc) and vals[1] == C.sizeof(B.PlanStruct)
+    got = [getattr(B.Desc, f).offset for f in fields_d] + [getattr(B.PlanStruct, f).offset for f in fields_p]
+    assert vals[2:] == got
+
+
+def _ws(desc):
+    return tr.load_library().moe_workspace_size(C.byref(desc))
+
+
+def test_workspace_size_and_desc_checks():
+    lib = tr.load_library()
+    good = tr.make_desc(T=16384, K=8, E=32, H=7168, I=2048)
+    n = _ws(good)
+    # T*K expanded rows of Xe and O (bf16) and of h, plus metadata
+    assert n >= 2 * 16384 * 8 * (2 * 7168 + 2048)
+    assert _ws(tr.make_desc(T=0, K=8, E=32, H=7168, I=2048)) > 0
+    bad = [dict(K=0), dict(K=33), dict(E=0), dict(E=1025), dict(T=-1)]
+    for kw in bad:
+        args = dict(T=64, K=2, E=8, H=256, I=128)
+        args.update(kw)
+        assert _ws(tr.make_desc(**args)) == 0, kw
+        assert lib.moe_last_error()
+    # bf16 needs H, I multiples of 64; fp32 needs H multiple of 8
+    assert _ws(tr.make_desc(T=8, K=2, E=4, H=100, I=64)) == 0
+    assert b"multiples of 64" in lib.moe_last_error()
+    assert _ws(tr.make_desc(T=8, K=2, E=4, H=104, I=72, dtype=torch.float32)) > 0
+    d = tr.make_desc(T=8, K=2, E=4, H=64, I=64, flags=3)
+    assert _ws(d) == 0
+
+
+def test_plan_rejects_bad_arguments_before_any_launch():
+    lib = tr.load_library()
+    d = tr.make_desc(T=64, K=2, E=8, H=256, I=128)
+    st = B.PlanStruct()
+    need = _ws(d)
+    fake = C.c_void_p(1 << 40)          # never dereferenced: checks fail first
+    assert lib.moe_plan(C.byref(d), fake, None, need, None, C.byref(st)) == -1
+    assert lib.moe_plan(C.byref(d), fake, C.c_void_p((1 << 40) + 8), need, None, C.byref(st)) == -1
+    assert lib.moe_plan(C.byref(d), fake, fake, need - 1, None, C.byref(st)) == -3
+    assert b"needs" in lib.moe_last_error()
+    assert lib.moe_plan(C.byref(d), None, fake, need, None, C.byref(st)) == -1
+    assert lib.moe_plan(C.byref(d), fake, fake, need, None, None) == -1
+    bad = tr.make_desc(T=64, K=2, E=8, H=256, I=128, dtype=7)
+    assert lib.moe_plan(C.byref(bad), fake, fake, need, None, C.byref(st)) == -1
+
+
+def test_entry_points_reject_null_plan():
+    lib = tr.load_library()
+    assert lib.moe_forward(None, None, None, None, None, None, None) == -1
+    assert lib.moe_expand(None, None, None) == -1
+    assert lib.moe_grouped_gemm(None, None, None, None) == -1
+    assert lib.moe_combine_reduce(None, None, None, None, None) == -1
+    assert lib.moe_plan_stats(None, None, None) == -1
+    empty = B.PlanStruct()            # no workspace
+    assert lib.moe_forward(C.byref(empty), None, None, None, None, None, None) == -1
+    assert b"workspace" in lib.moe_last_error()
+
+
+def test_forward_rejects_misaligned_buffers():
+    lib = tr.load_library()
+    st = B.PlanStruct()
+    st.d = tr.make_desc(T=64, K=2, E=8, H=256, I=128)
+    st.ws = C.c_void_p(1 << 40)
+    ok = C.c_void_p(1 << 41)
+    mis = C.c_void_p((1 << 41) + 4)
+    assert lib.moe_forward(C.byref(st), mis, None, ok, ok, ok, None) == -1
+    assert b"aligned" in lib.moe_last_error()
+    assert lib.moe_forward(C.byref(st), ok, None, None, ok, ok, None) == -1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "_HERE", str(tmp_path))
+    with pytest.raises(ImportError):
+        B.load_library()

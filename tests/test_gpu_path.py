@@ -1,0 +1,188 @@
+"""The HIP path through the C ABI vs the oracle.
+
+Element-by-element at sizes the oracle finishes in seconds (several tiles and
+ragged tails), and on sampled rows at the full workload sizes. Bars: expand is
+a bit copy (bit-exact); outputs within max|d| <= 1e-2 max|ref| + 1e-3 for
+bf16 and 1e-5 max|ref| for fp32."""
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import top_reduce_amd as tr
+from tests._gpu import as_f64, dev, host, sample_tokens, say, torch_dtype, upload
+from tests._util import max_err, tolerance
+
+pytestmark = pytest.mark.gpu
+
+# reduced shapes: several M tiles with ragged tails, several N tiles
+gen.custom_spec("mid", T=1024, K=8, E=8, G=64, H=1024, I=512, zipf_s=1.0, seed=7)
+gen.custom_spec("mid_small_experts", T=512, K=4, E=32, G=128, H=512, I=256, zipf_s=0.6, seed=8)
+gen.custom_spec("mid_f32", T=300, K=4, E=6, G=12, H=264, I=72, dtype="f32", zipf_s=0.5, seed=9)
+
+
+def _assert_close(got, ref, dtype, what):
+    err, tol = max_err(got, ref), tolerance(ref, dtype)
+    say(f"  {what}: max|d|={err:.3e} tol={tol:.3e} ratio={err / tol if tol else 0:.3f}")
+    assert err <= tol, f"{what}: max|d|={err} > tol={tol}"
+
+
+def _forward(wl, flags=0, y_alias=False, weights=True):
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch_dtype(wl), flags=flags)
+    y = d["x"] if y_alias else None
+    y = tr.forward(p, d["x"], d["w"] if weights else None, d["w1"], d["w2"], y=y)
+    torch.cuda.synchronize()
+    return p, host(y)
+
+
+@pytest.mark.parametrize("name,flags", [("c1", 0), ("mid_f32", 0), ("mid", 0),
+                                        ("mid", tr.FLAG_GEMM_FORCE_TILED),
+                                        ("mid", tr.FLAG_GEMM_FORCE_STREAM),
+                                        ("mid_small_experts", 0)])
+def test_forward_full_compare(name, flags):
+    say(f"forward {name} flags={flags}")
+    wl = gen.make_workload(name, with_weights=True)
+    _, y = _forward(wl, flags)
+    ref = oracle.forward(wl.x, wl.idx, wl.weights, wl.w1, wl.w2, wl.E)
+    _assert_close(as_f64(y), ref, wl.dtype, f"{name} y")
+    pad = ~(wl.idx >= 0).any(1)
+    assert (y[pad] == 0).all()
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 64])
+@pytest.mark.parametrize("variant", ["", "random"])
+def test_forward_c3_decode(T, variant):
+    say(f"forward c3 T={T} {variant}")
+    wl = gen.make_workload("c3", T=T, variant=variant, with_weights=True)
+    _, y = _forward(wl)
+    ref = oracle.forward(wl.x, wl.idx, wl.weights, wl.w1, wl.w2, wl.E)
+    _assert_close(as_f64(y), ref, wl.dtype, f"c3 T={T} y")
+    assert (y[~wl.real] == 0).all()
+
+
+def test_forward_c4_all_rows():
+    say("forward c4")
+    wl = gen.make_workload("c4", with_weights=True)
+    _, y = _forward(wl)
+    rows = np.nonzero((wl.idx >= 0).any(1))[0]
+    ref = oracle.forward(wl.x, wl.idx, wl.weights, wl.w1, wl.w2, wl.E, tokens=rows)
+    _assert_close(as_f64(y[rows]), ref, wl.dtype, "c4 y (rows with a local route)")
+    others = np.setdiff1d(np.arange(wl.T), rows)
+    assert (y[others] == 0).all()                       # exact +0 bits
+
+
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_forward_full_size_sampled(name):
+    say(f"forward {name} full size (sampled rows)")
+    wl = gen.make_workload(name, with_weights=True)
+    p, y = _forward(wl)
+    route = oracle.route(wl.idx, wl.E)
+    toks = sample_tokens(wl, route, 40)
+    ref = oracle.forward(wl.x, wl.idx, wl.weights, wl.w1, wl.w2, wl.E, tokens=toks)
+    _assert_close(as_f64(y[toks]), ref, wl.dtype, f"{name} y[{len(toks)} rows]")
+
+
+@pytest.mark.parametrize("name", ["mid", "c1"])
+def test_stages(name):
+    """expand bit-exact; O rows vs the oracle's per-route MLP; reduce."""
+    say(f"stages {name}")
+    wl = gen.make_workload(name, with_weights=True)
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch_dtype(wl))
+    route = oracle.route(wl.idx, wl.E)
+    R = route["R"]
+    tr.expand(p, d["x"])
+    v = p.views()
+    Xe = host(v["Xe"][:R])
+    assert np.array_equal(Xe, oracle.expand(wl.x, route["row_src"]))
+    tr.grouped_gemm(p, d["w1"], d["w2"])
+    O = host(v["O"][:R])
+    e_of_row = np.repeat(np.arange(wl.E), route["counts"])
+    O_ref = oracle.expert_rows(e_of_row, route["row_src"], wl.x, wl.w1, wl.w2)
+    _assert_close(as_f64(O), O_ref, wl.dtype, f"{name} O")
+    y = host(tr.combine_reduce(p, d["w"]))
+    _assert_close(as_f64(y), oracle.combine(route["row_map"], wl.weights, O), wl.dtype,
+                  f"{name} reduce of the GPU's O")
+
+
+@pytest.mark.parametrize("name", ["c5", "c4", "c1"])
+def test_combine_synthetic_outputs(name):
+    """Reduce alone on seeded expert outputs (not produced by the GPU)."""
+    say(f"combine {name}")
+    wl = gen.make_workload(name)
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch_dtype(wl))
+    route = oracle.route(wl.idx, wl.E)
+    O = gen.make_expert_outputs(wl.T * wl.K, wl.H, wl.dtype, seed=11)
+    Od = dev(O)
+    y = host(tr.combine_reduce(p, d["w"], expert_out=Od))
+    rows = np.arange(wl.T) if wl.T <= 2048 else sample_tokens(wl, route, 512)
+    ref = oracle.combine(route["row_map"][rows], wl.weights[rows], O)
+    _assert_close(as_f64(y[rows]), ref, wl.dtype, f"{name} combine")
+    # unit weights
+    y1 = host(tr.combine_reduce(p, None, expert_out=Od))
+    _assert_close(as_f64(y1[rows]), oracle.combine(route["row_map"][rows], None, O), wl.dtype,
+                  f"{name} combine w=1")
+
+
+def test_combine_closed_forms():
+    say("combine closed forms")
+    wl = gen.make_workload("c2", T=512)
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I)
+    route = oracle.route(wl.idx, wl.E)
+    # expert output 1 everywhere: y[t] = local weight sum, rounded once to bf16
+    ones = torch.ones((wl.T * wl.K, wl.H), dtype=torch.bfloat16, device="cuda")
+    y = host(tr.combine_reduce(p, d["w"], expert_out=ones))
+    wsum = np.where(wl.idx >= 0, wl.weights.astype(np.float64), 0).sum(1)
+    assert np.abs(as_f64(y) - wsum[:, None]).max() <= 2 ** -8 * wsum.max()
+    # identity expert + unit weight + top-1 routing: y == x bit for bit
+    idx1 = np.where(np.arange(wl.K)[None, :] == np.argmax(wl.idx >= 0, axis=1)[:, None], wl.idx, -1)
+    p1 = tr.plan(torch.from_numpy(idx1).cuda(), E=wl.E, H=wl.H, I=wl.I)
+    tr.expand(p1, d["x"])
+    y1 = tr.combine_reduce(p1, None, expert_out=p1.views()["Xe"])
+    assert torch.equal(y1.view(torch.int16), d["x"].view(torch.int16))
+    # non-local weights are never read (NaN there changes nothing)
+    wn = wl.weights.copy()
+    wn[wl.idx < 0] = np.nan
+    y2 = tr.combine_reduce(p, dev(wn), expert_out=ones)
+    assert torch.equal(y2.view(torch.int16), torch.from_numpy(y).view(torch.int16).cuda())
+
+
+def test_all_padding_gives_positive_zero():
+    say("all padding")
+    wl = gen.make_workload("c3", T=8, with_weights=True)
+    wl.idx[:] = -1
+    _, y = _forward(wl)
+    assert (y == 0).all()          # +0 bits
+
+
+def test_y_aliases_x():
+    say("y aliases x")
+    wl = gen.make_workload("mid", with_weights=True)
+    _, y_sep = _forward(wl)
+    _, y_al = _forward(wl, y_alias=True)
+    assert np.array_equal(y_sep, y_al)
+
+
+def test_forward_deterministic():
+    say("determinism")
+    wl = gen.make_workload("mid", with_weights=True)
+    _, a = _forward(wl)
+    _, b = _forward(wl)
+    assert np.array_equal(a, b)
+
+
+def test_error_convention_on_device():
+    wl = gen.make_workload("c1", with_weights=True)
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch.float32)
+    with pytest.raises(TypeError):
+        tr.forward(p, d["x"].to(torch.bfloat16), d["w"], d["w1"], d["w2"])
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(tr.TopReduceError) as ei:
+        tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch.float32, ws=small)
+    assert ei.value.status == -3

@@ -1,0 +1,30 @@
+"""top_reduce_amd: one GPU's share of an expert-parallel MoE FFN on MI355X.
+
+Route scan -> expand -> grouped SwiGLU GEMM -> weighted top-k reduce, as
+hand-written gfx950 HIP kernels behind the C ABI of ``libtopreduce.so``
+(``include/topreduce.h``). This package is the thin Python binding: it checks
+and marshals PyTorch tensors (device memory and streams only) and calls the
+library; every step of the path runs in the library's kernels. There is no
+fallback: if the library is not built, importing the binding's entry points
+raises.
+"""
+
+from ._binding import (  # noqa: F401
+    ABI_VERSION,
+    BF16,
+    F32,
+    FLAG_GEMM_FORCE_STREAM,
+    FLAG_GEMM_FORCE_TILED,
+    MoePlan,
+    TopReduceError,
+    combine_reduce,
+    expand,
+    forward,
+    grouped_gemm,
+    lib_path,
+    load_library,
+    make_desc,
+    plan,
+    plan_stats,
+    workspace_size,
+)

@@ -1,0 +1,239 @@
+// C ABI of libtopreduce: argument checks, workspace layout, and the launch
+// sequence of the hot path. Every entry point validates on the host and then
+// only enqueues kernels on the caller's stream; nothing here allocates device
+// memory or synchronises (moe_plan_stats excepted, by design).
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "tr_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+tr_status fail(tr_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tr_status ok() {
+  g_err[0] = '\0';
+  return TR_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+tr_status check_desc(const tr_moe_desc* d) {
+  if (!d) return fail(TR_EINVAL, "desc is NULL");
+  if (d->T < 0) return fail(TR_EINVAL, "T must be >= 0 (got %lld)", (long long)d->T);
+  if (d->K < 1 || d->K > tr::kMaxK) return fail(TR_EINVAL, "K must be in [1, %d] (got %d)", tr::kMaxK, d->K);
+  if (d->E < 1 || d->E > tr::kMaxE) return fail(TR_EINVAL, "E must be in [1, %d] (got %d)", tr::kMaxE, d->E);
+  if (d->H < 1 || d->I < 1) return fail(TR_EINVAL, "H and I must be >= 1");
+  if (d->dtype != TR_BF16 && d->dtype != TR_F32) return fail(TR_EINVAL, "unknown dtype %d", d->dtype);
+  if (d->idx_dtype != TR_IDX_I32 && d->idx_dtype != TR_IDX_I64)
+    return fail(TR_EINVAL, "unknown idx_dtype %d", d->idx_dtype);
+  const int32_t known = TR_FLAG_GEMM_FORCE_TILED | TR_FLAG_GEMM_FORCE_STREAM;
+  if (d->flags & ~known) return fail(TR_EINVAL, "unknown flags 0x%x", d->flags);
+  if ((d->flags & known) == known) return fail(TR_EINVAL, "both GEMM force flags set");
+  if (d->H > (1 << 24) || d->I > (1 << 24)) return fail(TR_EUNSUPPORTED, "H and I must be <= 2^24");
+  if (d->T > (int64_t(1) << 31) / d->K) return fail(TR_EUNSUPPORTED, "T*K must be < 2^31");
+  if (d->expert_begin > (int64_t(1) << 62) || d->expert_begin < -(int64_t(1) << 62))
+    return fail(TR_EINVAL, "expert_begin out of range");
+  if (d->dtype == TR_BF16) {
+    if (d->H % 64 || d->I % 64)
+      return fail(TR_EUNSUPPORTED, "bf16 needs H and I multiples of 64 (got H=%lld I=%lld)",
+                  (long long)d->H, (long long)d->I);
+  } else {
+    if (d->H % 8) return fail(TR_EUNSUPPORTED, "fp32 needs H a multiple of 8 (got %lld)", (long long)d->H);
+  }
+  return TR_OK;
+}
+
+struct Layout {
+  int64_t R_cap;
+  int blocks, rpb;
+  size_t stats, counts, offsets, row_map, row_src, row_k, scan_tmp, Xe, h, O, total;
+};
+
+Layout layout(const tr_moe_desc& d) {
+  Layout L{};
+  // one expanded row per local slot; a row may name the same expert twice
+  L.R_cap = d.T * d.K;
+  tr::route_scan_geometry(d.T, d.K, &L.blocks, &L.rpb);
+  const size_t es = d.dtype == TR_BF16 ? 2 : 4;
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = up(o + bytes); return at; };
+  L.stats = take(16 * sizeof(int32_t));
+  L.counts = take(sizeof(int32_t) * d.E);
+  L.offsets = take(sizeof(int32_t) * (d.E + 1));
+  L.row_map = take(sizeof(int32_t) * d.T * d.K);
+  L.row_src = take(sizeof(int32_t) * L.R_cap);
+  L.row_k = take(sizeof(int32_t) * L.R_cap);
+  L.scan_tmp = take(sizeof(int32_t) * static_cast<size_t>(L.blocks) * (d.E + 2));
+  L.Xe = take(es * L.R_cap * d.H);
+  L.h = take(es * L.R_cap * d.I);
+  L.O = take(es * L.R_cap * d.H);
+  L.total = o;
+  return L;
+}
+
+tr_status check_plan(const tr_moe_plan* p) {
+  if (!p) return fail(TR_EINVAL, "plan is NULL");
+  if (!p->ws) return fail(TR_EINVAL, "plan has no workspace (was moe_plan called?)");
+  return check_desc(&p->d);
+}
+
+tr_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TR_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+namespace tr {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev < 64 ? dev : 63;
+  int v = cache[slot].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  cache[slot].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace tr
+
+extern "C" {
+
+size_t moe_workspace_size(const tr_moe_desc* desc) {
+  if (check_desc(desc) != TR_OK) return 0;
+  ok();
+  return layout(*desc).total;
+}
+
+tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size_t ws_bytes,
+                   hipStream_t stream, tr_moe_plan* out) {
+  tr_status s = check_desc(desc);
+  if (s != TR_OK) return s;
+  if (!out) return fail(TR_EINVAL, "out plan is NULL");
+  if (!ws) return fail(TR_EINVAL, "workspace is NULL");
+  if (!aligned(ws, kAlign)) return fail(TR_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+  const Layout L = layout(*desc);
+  if (ws_bytes < L.total)
+    return fail(TR_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+  const size_t isz = desc->idx_dtype == TR_IDX_I64 ? 8 : 4;
+  if (desc->T > 0 && !topk_idx) return fail(TR_EINVAL, "topk_idx is NULL");
+  if (topk_idx && !aligned(topk_idx, isz)) return fail(TR_EINVAL, "topk_idx misaligned");
+
+  tr_moe_plan p;
+  memset(&p, 0, sizeof p);
+  p.d = *desc;
+  p.R_cap = L.R_cap;
+  p.ws = ws;
+  p.ws_bytes = ws_bytes;
+  char* b = static_cast<char*>(ws);
+  p.stats = reinterpret_cast<int32_t*>(b + L.stats);
+  p.counts = reinterpret_cast<int32_t*>(b + L.counts);
+  p.offsets = reinterpret_cast<int32_t*>(b + L.offsets);
+  p.row_map = reinterpret_cast<int32_t*>(b + L.row_map);
+  p.row_src = reinterpret_cast<int32_t*>(b + L.row_src);
+  p.row_k = reinterpret_cast<int32_t*>(b + L.row_k);
+  p.scan_tmp = reinterpret_cast<int32_t*>(b + L.scan_tmp);
+  p.Xe = b + L.Xe;
+  p.h = b + L.h;
+  p.O = b + L.O;
+  p.scan_blocks = L.blocks;
+  p.scan_rows_per_block = L.rpb;
+  // T == 0 still runs the (one-block) scan so counts, offsets and stats are
+  // defined as zeros.
+  s = hip_status(tr::route_scan(p, topk_idx, stream), "moe_route_scan launch");
+  if (s != TR_OK) return s;
+  *out = p;
+  return ok();
+}
+
+static tr_status check_buf(const void* p, const char* name, bool needed) {
+  if (!needed) return TR_OK;
+  if (!p) return fail(TR_EINVAL, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(TR_EINVAL, "%s must be 16-byte aligned", name);
+  return TR_OK;
+}
+
+tr_status moe_expand(const tr_moe_plan* plan, const void* x, hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  const bool any = plan->d.T > 0;
+  if ((s = check_buf(x, "x", any)) != TR_OK) return s;
+  if (!any) return ok();
+  return hip_status(tr::expand(*plan, x, stream), "moe_expand launch");
+}
+
+tr_status moe_grouped_gemm(const tr_moe_plan* plan, const void* w1, const void* w2,
+                           hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  const bool any = plan->d.T > 0;
+  if ((s = check_buf(w1, "w1", any)) != TR_OK) return s;
+  if ((s = check_buf(w2, "w2", any)) != TR_OK) return s;
+  if (!any) return ok();
+  return hip_status(tr::grouped_gemm(*plan, w1, w2, stream), "moe_grouped_gemm launch");
+}
+
+tr_status moe_combine_reduce(const tr_moe_plan* plan, const void* expert_out,
+                             const float* topk_weights, void* y, hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  const bool any = plan->d.T > 0;
+  if ((s = check_buf(y, "y", any)) != TR_OK) return s;
+  if (expert_out && !aligned(expert_out, 16)) return fail(TR_EINVAL, "expert_out must be 16-byte aligned");
+  if (topk_weights && !aligned(topk_weights, 4)) return fail(TR_EINVAL, "topk_weights misaligned");
+  if (!any) return ok();
+  return hip_status(tr::combine_reduce(*plan, expert_out, topk_weights, y, stream),
+                    "moe_combine_reduce launch");
+}
+
+tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_weights,
+                      const void* w1, const void* w2, void* y, hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  const bool any = plan->d.T > 0;
+  if ((s = check_buf(x, "x", any)) != TR_OK) return s;
+  if ((s = check_buf(w1, "w1", any)) != TR_OK) return s;
+  if ((s = check_buf(w2, "w2", any)) != TR_OK) return s;
+  if ((s = check_buf(y, "y", any)) != TR_OK) return s;
+  if (topk_weights && !aligned(topk_weights, 4)) return fail(TR_EINVAL, "topk_weights misaligned");
+  if (!any) return ok();
+  if ((s = hip_status(tr::expand(*plan, x, stream), "moe_expand launch")) != TR_OK) return s;
+  if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, stream), "moe_grouped_gemm launch")) != TR_OK)
+    return s;
+  return hip_status(tr::combine_reduce(*plan, nullptr, topk_weights, y, stream),
+                    "moe_combine_reduce launch");
+}
+
+tr_status moe_plan_stats(const tr_moe_plan* plan, int32_t* host_out, hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  if (!host_out) return fail(TR_EINVAL, "host_out is NULL");
+  hipError_t e = hipMemcpyAsync(host_out, plan->stats, 4 * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return hip_status(e, "moe_plan_stats");
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int32_t moe_abi_version(void) { return TR_ABI_VERSION; }
+
+}  // extern "C"

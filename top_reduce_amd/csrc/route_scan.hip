@@ -1,0 +1,249 @@
+// moe_route_scan: per-expert histogram, segment offsets and the stable maps
+// between received slots (t, k) and expanded rows.
+//
+// DeepEP issue #48 ("How to apply MoE MLP to recv_x ... num_expert_per_rank >
+// 1", answers): a grouped GEMM needs each token copied once per local expert,
+// in expert-contiguous segments, and the reduction afterwards must find every
+// copy again. Slot (t, k) is local when its id lies in [expert_begin,
+// expert_begin + E); the others (-1 padding and other ranks' experts, DeepEP
+// issue #760 repro) are skipped. Inside a segment rows follow the received
+// order: token-major, then slot.
+//
+// Design (one GPU, no host sync):
+//  - rows are cut into fixed blocks; kernel `route_count` writes each block's
+//    per-expert counts (plus ignored slots and rows with a local route);
+//  - kernel `route_scatter` has every block sum the partials into totals and
+//    its own starting position per expert, then rank its slots with wave
+//    ballots: lanes holding the same expert find each other by matching the
+//    expert id bit by bit, their rank is a popcount of the lower peers, and
+//    waves are chained in LDS. Positions never depend on atomic order, so the
+//    maps are bit-exact and deterministic.
+//  - a small input (T*K <= 4096) runs as one block that counts for itself:
+//    one launch instead of two.
+#include "tr_device.h"
+#include "tr_internal.h"
+
+namespace tr {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+template <typename IdxT>
+__device__ __forceinline__ int local_of(IdxT id, int64_t eb, int E) {
+  const int64_t e = static_cast<int64_t>(id) - eb;
+  return (e >= 0 && e < E) ? static_cast<int>(e) : E;  // E: not local
+}
+
+// Adds the slots of rows [r0, r1) to cnt[0..E+2): per-expert counts, then
+// cnt[E] = ignored slots, cnt[E+1] = rows with at least one local slot.
+template <typename IdxT>
+__device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1, int K,
+                           int64_t eb, int E, int* cnt) {
+  const int64_t s0 = r0 * K, s1 = r1 * K;
+  for (int64_t base = s0; base < s1; base += kThreads) {
+    const int64_t s = base + threadIdx.x;
+    const bool in = s < s1;
+    const int e = in ? local_of(idx[s], eb, E) : E;
+    if (e < E) atomicAdd(&cnt[e], 1);
+    const uint64_t ign = __ballot(in && e == E);
+    if (lane_id() == 0 && ign) atomicAdd(&cnt[E], __popcll(ign));
+  }
+  for (int64_t base = r0; base < r1; base += kThreads) {
+    const int64_t r = base + threadIdx.x;
+    bool any = false;
+    if (r < r1)
+      for (int k = 0; k < K; ++k) any |= local_of(idx[r * K + k], eb, E) < E;
+    const uint64_t m = __ballot(any);
+    if (lane_id() == 0 && m) atomicAdd(&cnt[E + 1], __popcll(m));
+  }
+}
+
+template <typename IdxT>
+__global__ __launch_bounds__(kThreads) void route_count(const IdxT* __restrict__ idx, int64_t T,
+                                                        int K, int64_t eb, int E, int rpb,
+                                                        int* __restrict__ hist) {
+  extern __shared__ int cnt[];
+  for (int i = threadIdx.x; i < E + 2; i += kThreads) cnt[i] = 0;
+  __syncthreads();
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rpb;
+  const int64_t r1 = r0 + rpb < T ? r0 + rpb : T;
+  count_rows(idx, r0, r1, K, eb, E, cnt);
+  __syncthreads();
+  for (int i = threadIdx.x; i < E + 2; i += kThreads) hist[blockIdx.x * (E + 2) + i] = cnt[i];
+}
+
+// kSelf: single block, counts its own rows instead of reading `hist`.
+template <typename IdxT, bool kSelf>
+__global__ __launch_bounds__(kThreads) void route_scatter(
+    const IdxT* __restrict__ idx, int64_t T, int K, int64_t eb, int E, int rpb, int nblocks,
+    const int* __restrict__ hist, int* __restrict__ counts, int* __restrict__ offsets,
+    int* __restrict__ row_map, int* __restrict__ row_src, int* __restrict__ row_k,
+    int* __restrict__ stats) {
+  extern __shared__ int sh[];
+  int* base = sh;                       // [E] first row of this block's slots per expert
+  int* running = base + E;              // [E] rows taken so far by this block
+  int* wcnt = running + E;              // [kWaves][E + 1] per-wave counts of a round
+  int* cnt = wcnt + kWaves * (E + 1);   // [E + 2] own counts (kSelf)
+  int* tmp = cnt + (E + 2);             // [kWaves] scan scratch
+  int* misc = tmp + kWaves;             // [4]
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rpb;
+  const int64_t r1 = r0 + rpb < T ? r0 + rpb : T;
+
+  for (int i = tid; i < kWaves * (E + 1); i += kThreads) wcnt[i] = 0;
+  if (tid < 4) misc[tid] = 0;
+  if (kSelf) {
+    for (int i = tid; i < E + 2; i += kThreads) cnt[i] = 0;
+    __syncthreads();
+    count_rows(idx, r0, r1, K, eb, E, cnt);
+  }
+  __syncthreads();
+
+  // 1. totals per expert, this block's prior count, segment offsets.
+  const int per = (E + kThreads - 1) / kThreads;  // experts per thread (<= 4)
+  int tsum = 0;
+  int tot[4], pri[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    tot[j] = 0;
+    pri[j] = 0;
+    const int e = tid * per + j;
+    if (j < per && e < E) {
+      if (kSelf) {
+        tot[j] = cnt[e];
+      } else {
+        for (int b = 0; b < nblocks; ++b) {
+          const int c = hist[b * (E + 2) + e];
+          tot[j] += c;
+          if (b < static_cast<int>(blockIdx.x)) pri[j] += c;
+        }
+      }
+      tsum += tot[j];
+    }
+  }
+  int R = 0;
+  int off = block_exclusive_scan<kThreads>(tsum, tmp, &R);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = tid * per + j;
+    if (j < per && e < E) {
+      base[e] = off + pri[j];
+      running[e] = 0;
+      if (blockIdx.x == 0) {
+        counts[e] = tot[j];
+        offsets[e] = off;
+        if (tot[j] == 0) atomicAdd(&misc[0], 1);
+      }
+      off += tot[j];
+    }
+  }
+  if (blockIdx.x == 0) {
+    // ignored slots and rows with a local route, summed over blocks
+    if (kSelf) {
+      if (tid == 0) { misc[1] = cnt[E]; misc[2] = cnt[E + 1]; }
+    } else {
+      int ign = 0, tl = 0;
+      for (int b = tid; b < nblocks; b += kThreads) {
+        ign += hist[b * (E + 2) + E];
+        tl += hist[b * (E + 2) + E + 1];
+      }
+      if (ign) atomicAdd(&misc[1], ign);
+      if (tl) atomicAdd(&misc[2], tl);
+    }
+  }
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0) {
+    offsets[E] = R;
+    stats[0] = R;
+    stats[1] = misc[2];
+    stats[2] = misc[1];
+    stats[3] = misc[0];
+  }
+
+  // 2. stable ranks, one round of kThreads slots at a time.
+  const int nbits = 32 - __clz(E);  // bits of the values 0..E
+  const int64_t s0 = r0 * K, s1 = r1 * K;
+  for (int64_t rb = s0; rb < s1; rb += kThreads) {
+    const int64_t s = rb + tid;
+    const bool in = s < s1;
+    const int e = in ? local_of(idx[s], eb, E) : E;
+    const bool valid = e < E;
+    uint64_t peers = __ballot(1);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    const int rank = popc_below(peers);
+    const bool leader = rank == 0;
+    if (leader && valid) wcnt[wave * (E + 1) + e] = __popcll(peers);
+    __syncthreads();
+    int row = -1;
+    if (valid) {
+      int before = 0;
+      for (int w = 0; w < wave; ++w) before += wcnt[w * (E + 1) + e];
+      row = base[e] + running[e] + before + rank;
+    }
+    __syncthreads();
+    if (leader && valid) {
+      atomicAdd(&running[e], wcnt[wave * (E + 1) + e]);
+      wcnt[wave * (E + 1) + e] = 0;
+    }
+    __syncthreads();
+    if (in) {
+      row_map[s] = row;
+      if (valid) {
+        row_src[row] = static_cast<int>(s / K);
+        row_k[row] = static_cast<int>(s % K);
+      }
+    }
+  }
+}
+
+template <typename IdxT>
+hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
+  const tr_moe_desc& d = p.d;
+  const int E = d.E, K = d.K;
+  const int nb = p.scan_blocks, rpb = p.scan_rows_per_block;
+  const size_t sh_scatter = sizeof(int) * (2 * E + kWaves * (E + 1) + (E + 2) + kWaves + 4);
+  if (nb == 1) {
+    hipLaunchKernelGGL((route_scatter<IdxT, true>), dim3(1), dim3(kThreads), sh_scatter, st, idx,
+                       d.T, K, d.expert_begin, E, rpb, nb, p.scan_tmp, p.counts, p.offsets,
+                       p.row_map, p.row_src, p.row_k, p.stats);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((route_count<IdxT>), dim3(nb), dim3(kThreads), sizeof(int) * (E + 2), st,
+                     idx, d.T, K, d.expert_begin, E, rpb, p.scan_tmp);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((route_scatter<IdxT, false>), dim3(nb), dim3(kThreads), sh_scatter, st, idx,
+                     d.T, K, d.expert_begin, E, rpb, nb, p.scan_tmp, p.counts, p.offsets,
+                     p.row_map, p.row_src, p.row_k, p.stats);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t route_scan(const tr_moe_plan& p, const void* idx, hipStream_t st) {
+  if (p.d.idx_dtype == TR_IDX_I64) return launch(p, static_cast<const int64_t*>(idx), st);
+  return launch(p, static_cast<const int32_t*>(idx), st);
+}
+
+void route_scan_geometry(int64_t T, int K, int* blocks, int* rows_per_block) {
+  // One block for small inputs; otherwise ~1024 slots per block, at most
+  // kMaxScanBlocks blocks.
+  if (T * K <= 4096) {
+    *blocks = 1;
+    *rows_per_block = static_cast<int>(T > 0 ? T : 1);
+    return;
+  }
+  int64_t rpb = cdiv(1024, K);
+  if (cdiv(T, rpb) > kMaxScanBlocks) rpb = cdiv(T, kMaxScanBlocks);
+  *rows_per_block = static_cast<int>(rpb);
+  *blocks = static_cast<int>(cdiv(T, rpb));
+}
+
+}  // namespace tr

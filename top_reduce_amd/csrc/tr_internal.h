@@ -1,0 +1,26 @@
+// Internal launchers of libtopreduce (host side). Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "topreduce.h"
+
+namespace tr {
+
+constexpr int kMaxScanBlocks = 256;
+constexpr int kMaxK = 32;
+constexpr int kMaxE = 1024;
+// Experts with at most this many routes go to the weight-streaming GEMM.
+constexpr int kStreamMaxRows = 32;
+
+hipError_t route_scan(const tr_moe_plan& p, const void* idx, hipStream_t st);
+void route_scan_geometry(int64_t T, int K, int* blocks, int* rows_per_block);
+hipError_t expand(const tr_moe_plan& p, const void* x, hipStream_t st);
+hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, hipStream_t st);
+hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const float* w, void* y,
+                          hipStream_t st);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace tr
