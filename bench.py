@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Throughput of one GPU's share of the expert-parallel MoE FFN on MI355X.
+
+One step = the whole hot path on one batch: moe_plan (route scan) +
+moe_forward (expand, grouped SwiGLU GEMM up/down, weighted top-k reduce), on
+synthetic inputs already resident in HBM. Default workload: the prefill shape
+(16384 received tokens, H=7168, I=2048, 32 local experts of 256, top-8, Zipf
+s=1.0 popularity), bf16.
+
+Prints ONE JSON line: tokens/s over the timed steps, the roofline of the
+dominant kernel (HIP events on the stream the kernels run on), per-stage
+rates, a sampled parity check and the CPU oracle's rate on a bounded sample
+of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config c5] [--gpus 1]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at 1 GPU; grouped-GEMM % MFMA peak; expand/reduce % HBM BW"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+WORKLOAD_NAMES = {
+    "c1": "tiny fp32: T=64, H=256, I=128, 8 experts, top-2",
+    "c2": "EP16 rank share: T=4096, H=7168, I=2048, 16 local of 256 experts, top-8 uniform",
+    "c3": "low-batch decode: H=3584, I=2048, 28 local of 896 experts, top-16 stride, 1 real row in 8",
+    "c4": "DP-padded skew: 960-row buffer (127 real), H=7168, I=2048, 32 local of 256, Zipf s=1.2",
+    "c5": "prefill: T=16384, H=7168, I=2048, 32 local of 256 experts, top-8, Zipf s=1.0",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c5", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--T", type=int, default=None, help="row count override (c3: 1, 2, 4, 8, 64)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target length of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--loop-only", action="store_true",
+                    help="only warmup + timed steps (for profiler runs)")
+    return ap.parse_args()
+
+
+def kernel_source_hash(name: str) -> str:
+    path = os.path.join(ROOT, "top_reduce_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel: str, config: str, src: str):
+    """HBM bytes per launch measured by rocprofv3 counters (profiles/), or None
+    when absent or taken on another version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{config}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_h = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_h and m_b) or m_h.group(1) != kernel_source_hash(src):
+        return None
+    return float(m_b.group(1))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}, WORLD_SIZE {world}); this "
+              "build has no multi-GPU path: sharding is by expert range, one process per GPU, "
+              "each running this same single-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gen
+    import top_reduce_amd as tr
+
+    tr.load_library()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    wl = gen.make_workload(args.config, T=args.T, with_weights=True)
+    log(f"[bench] generated {args.config} T={wl.T} in {time.time() - t0:.1f}s")
+    bf16 = wl.dtype == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    idx = torch.from_numpy(wl.idx).to(dev)
+    x, w = up(wl.x), torch.from_numpy(wl.weights).to(dev)
+    w1, w2 = up(wl.w1), up(wl.w2)
+    y = torch.empty((wl.T, wl.H), dtype=tdt, device=dev)
+    desc = tr.make_desc(wl.T, wl.K, wl.E, wl.H, wl.I, tdt, torch.int64)
+    ws = torch.empty(tr.workspace_size(desc), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        p = tr.plan(idx, E=wl.E, H=wl.H, I=wl.I, dtype=tdt, ws=ws, stream=stream)
+        tr.forward(p, x, w, w1, w2, y=y, stream=stream)
+        return p
+
+    p = step()
+    R, T_loc, _, n_empty = tr.plan_stats(p)
+    real_rows = int(wl.real.sum())
+    log(f"[bench] R={R} T_loc={T_loc} real_rows={real_rows} empty_experts={n_empty}")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    tokens_per_s = real_rows * args.steps / (ms_total / 1e3)
+    log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (wall {wall / args.steps * 1e3:.4f}), "
+        f"{tokens_per_s:.4e} tokens/s")
+    if args.loop_only:
+        print(json.dumps({"metric": METRIC, "value": tokens_per_s, "unit": "tokens/s",
+                          "ms_per_step": ms_step, "loop_only": True}), flush=True)
+        return
+
+    # Per-stage device time: each stage alone, args.steps launches between two
+    # events on the same stream.
+    def timed(fn, n=None):
+        n = n or args.steps
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3          # us per launch
+
+    us = {
+        "route_scan": timed(lambda: tr.plan(idx, E=wl.E, H=wl.H, I=wl.I, dtype=tdt, ws=ws, stream=stream)),
+        "expand": timed(lambda: tr.expand(p, x, stream=stream)),
+        "gemm_up": timed(lambda: tr.grouped_gemm_up(p, w1, stream=stream)),
+        "gemm_down": timed(lambda: tr.grouped_gemm_down(p, w2, stream=stream)),
+        "combine_reduce": timed(lambda: tr.combine_reduce(p, w, y=y, stream=stream)),
+    }
+    b = 2 if bf16 else 4
+    H, I, T, K = wl.H, wl.I, wl.T, wl.K
+    peak_mm = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
+    work = {
+        # algorithmic bytes / flops per launch
+        "expand": ("hbm", (T_loc + R) * H * b + 4 * R),
+        "gemm_up": ("mfma" if bf16 else "alu", 4.0 * R * H * I),
+        "gemm_down": ("mfma" if bf16 else "alu", 2.0 * R * H * I),
+        "combine_reduce": ("hbm", R * H * b + T * H * b + 8 * T * K),
+    }
+    stages = {"route_scan": {"us": us["route_scan"]}}
+    for k, (bound, amount) in work.items():
+        t_s = us[k] / 1e6
+        if bound == "hbm":
+            ach = amount / t_s / 1e9
+            stages[k] = {"us": us[k], "bound": "hbm", "achieved": ach, "unit": "GB/s",
+                         "peak": PEAK_HBM_GBS, "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": amount}
+        else:
+            ach = amount / t_s / 1e12
+            stages[k] = {"us": us[k], "bound": bound, "achieved": ach, "unit": "TFLOP/s",
+                         "peak": peak_mm, "frac": ach / peak_mm, "algorithmic_flops": amount}
+    dominant = max(work, key=lambda k: us[k])
+    dom = stages[dominant]
+    src = {"expand": "expand.hip", "gemm_up": "grouped_gemm.hip", "gemm_down": "grouped_gemm.hip",
+           "combine_reduce": "combine_reduce.hip"}[dominant]
+    traffic = stored_traffic(dominant, args.config, src)
+    roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"],
+                "peak": dom["peak"], "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic}
+    for k, v in stages.items():
+        log(f"[bench] {k:15s} {v['us']:10.2f} us" +
+            (f"  {v['achieved']:9.1f} {v['unit']}  {100 * v['frac']:5.1f}% of peak" if "frac" in v else ""))
+
+    result = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
+        "config": {"workload": f"{args.config} {WORKLOAD_NAMES[args.config]}", "T": T,
+                   "real_rows": real_rows, "K": K, "E_local": wl.E, "E_global": wl.G, "H": H,
+                   "I": I, "R": R, "T_loc": T_loc, "empty_experts": n_empty, "seed": wl.seed,
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "stages": stages,
+    }
+
+    # Sampled parity and the CPU oracle baseline on a bounded sample.
+    if not (args.no_check and args.no_cpu_baseline):
+        import oracle
+        nthreads = oracle.threads()
+        routes_per_row = max(R / max(real_rows, 1), 1e-9)
+        probe = np.arange(min(16, T))
+        t1 = time.perf_counter()
+        oracle.forward(wl.x, wl.idx, wl.weights, wl.w1, wl.w2, wl.E, tokens=probe)
+        per_route = (time.perf_counter() - t1) / max(int((wl.idx[probe] >= 0).sum()), 1)
+        n = int(args.cpu_seconds / max(per_route * routes_per_row, 1e-9))
+        n = min(T, max(16, n))
+        toks = np.arange(n)
+        t1 = time.perf_counter()
+        ref = oracle.forward(wl.x, wl.idx, wl.weights, wl.w1, wl.w2, wl.E, tokens=toks)
+        cpu_s = time.perf_counter() - t1
+        n_real = int(wl.real[toks].sum())
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = {
+                "value": n_real / cpu_s, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+                "seconds": cpu_s,
+                "sample": f"first {n} of {T} rows of the same workload ({n_real} real rows, "
+                          f"{int((wl.idx[toks] >= 0).sum())} local routes), fp64 oracle, "
+                          f"{nthreads} OpenMP threads"}
+            log(f"[bench] cpu oracle: {n_real / cpu_s:.2f} tokens/s on {nthreads} threads ({cpu_s:.1f}s)")
+        if not args.no_check:
+            yh = y[:n].float().cpu().numpy().astype(np.float64)
+            err = float(np.abs(yh - ref).max())
+            tol = (1e-2 * float(np.abs(ref).max()) + 1e-3) if bf16 else 1e-5 * float(np.abs(ref).max())
+            result["parity"] = {"rows": n, "max_abs_err": err, "tol": tol, "ratio": err / tol if tol else 0.0,
+                                "ok": err <= tol}
+            log(f"[bench] parity on {n} rows: max|d|={err:.3e} tol={tol:.3e}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

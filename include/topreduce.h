@@ -137,6 +137,13 @@ tr_status moe_expand(const tr_moe_plan* plan, const void* x, hipStream_t stream)
 tr_status moe_grouped_gemm(const tr_moe_plan* plan, const void* w1, const void* w2,
                            hipStream_t stream);
 
+/* The two halves of moe_grouped_gemm, for callers that fuse or time them
+ * separately: _up computes h from the plan's Xe and w1 (GEMM1 with the SwiGLU
+ * epilogue), _down computes O from h and w2. Running _up then _down on one
+ * stream is exactly moe_grouped_gemm. */
+tr_status moe_grouped_gemm_up(const tr_moe_plan* plan, const void* w1, hipStream_t stream);
+tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStream_t stream);
+
 /* Weighted top-k reduce (DeepEP issue #48: the reduction before the combine
  * all-to-all; DeepEP issue #760: the combine epilogue, one row per received
  * token): y[t] = sum over k ascending with row_map[t][k] >= 0 of

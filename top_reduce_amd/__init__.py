@@ -21,6 +21,8 @@ from ._binding import (  # noqa: F401
     expand,
     forward,
     grouped_gemm,
+    grouped_gemm_down,
+    grouped_gemm_up,
     lib_path,
     load_library,
     make_desc,

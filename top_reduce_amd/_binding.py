@@ -76,6 +76,10 @@ def load_library():
     lib.moe_expand.argtypes = [C.POINTER(PlanStruct), vp, vp]
     lib.moe_grouped_gemm.restype = st
     lib.moe_grouped_gemm.argtypes = [C.POINTER(PlanStruct), vp, vp, vp]
+    lib.moe_grouped_gemm_up.restype = st
+    lib.moe_grouped_gemm_up.argtypes = [C.POINTER(PlanStruct), vp, vp]
+    lib.moe_grouped_gemm_down.restype = st
+    lib.moe_grouped_gemm_down.argtypes = [C.POINTER(PlanStruct), vp, vp]
     lib.moe_combine_reduce.restype = st
     lib.moe_combine_reduce.argtypes = [C.POINTER(PlanStruct), vp, vp, vp, vp]
     lib.moe_plan_stats.restype = st
@@ -246,6 +250,20 @@ def grouped_gemm(p: MoePlan, w1: torch.Tensor, w2: torch.Tensor, stream=None) ->
     _check(load_library().moe_grouped_gemm(C.byref(p.struct), C.c_void_p(w1p or None),
                                            C.c_void_p(w2p or None),
                                            _stream_ptr(stream, p.ws.device)))
+
+
+def grouped_gemm_up(p: MoePlan, w1: torch.Tensor, stream=None) -> None:
+    d = p.desc
+    w1p = _dev_tensor(w1, "w1", _torch_dtype(d.dtype), (d.E, 2 * d.I, d.H))
+    _check(load_library().moe_grouped_gemm_up(C.byref(p.struct), C.c_void_p(w1p or None),
+                                              _stream_ptr(stream, p.ws.device)))
+
+
+def grouped_gemm_down(p: MoePlan, w2: torch.Tensor, stream=None) -> None:
+    d = p.desc
+    w2p = _dev_tensor(w2, "w2", _torch_dtype(d.dtype), (d.E, d.H, d.I))
+    _check(load_library().moe_grouped_gemm_down(C.byref(p.struct), C.c_void_p(w2p or None),
+                                                _stream_ptr(stream, p.ws.device)))
 
 
 def combine_reduce(p: MoePlan, topk_weights: Optional[torch.Tensor],

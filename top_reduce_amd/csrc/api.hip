@@ -189,7 +189,28 @@ tr_status moe_grouped_gemm(const tr_moe_plan* plan, const void* w1, const void* 
   if ((s = check_buf(w1, "w1", any)) != TR_OK) return s;
   if ((s = check_buf(w2, "w2", any)) != TR_OK) return s;
   if (!any) return ok();
-  return hip_status(tr::grouped_gemm(*plan, w1, w2, stream), "moe_grouped_gemm launch");
+  return hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream),
+                    "moe_grouped_gemm launch");
+}
+
+tr_status moe_grouped_gemm_up(const tr_moe_plan* plan, const void* w1, hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  const bool any = plan->d.T > 0;
+  if ((s = check_buf(w1, "w1", any)) != TR_OK) return s;
+  if (!any) return ok();
+  return hip_status(tr::grouped_gemm(*plan, w1, nullptr, tr::kGemmUp, stream),
+                    "moe_grouped_gemm_up launch");
+}
+
+tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  const bool any = plan->d.T > 0;
+  if ((s = check_buf(w2, "w2", any)) != TR_OK) return s;
+  if (!any) return ok();
+  return hip_status(tr::grouped_gemm(*plan, nullptr, w2, tr::kGemmDown, stream),
+                    "moe_grouped_gemm_down launch");
 }
 
 tr_status moe_combine_reduce(const tr_moe_plan* plan, const void* expert_out,
@@ -217,7 +238,8 @@ tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_
   if (topk_weights && !aligned(topk_weights, 4)) return fail(TR_EINVAL, "topk_weights misaligned");
   if (!any) return ok();
   if ((s = hip_status(tr::expand(*plan, x, stream), "moe_expand launch")) != TR_OK) return s;
-  if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, stream), "moe_grouped_gemm launch")) != TR_OK)
+  if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream),
+                      "moe_grouped_gemm launch")) != TR_OK)
     return s;
   return hip_status(tr::combine_reduce(*plan, nullptr, topk_weights, y, stream),
                     "moe_combine_reduce launch");

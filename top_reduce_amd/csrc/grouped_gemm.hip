@@ -472,7 +472,8 @@ __global__ __launch_bounds__(kThreads) void gemm_f32(GemmArgs a, int I) {
 
 }  // namespace
 
-hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, hipStream_t st) {
+hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, int parts,
+                        hipStream_t st) {
   const tr_moe_desc& d = p.d;
   if (d.T == 0) return hipSuccess;
   const int cus = device_cu_count();
@@ -480,19 +481,25 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, hi
                    : (d.flags & TR_FLAG_GEMM_FORCE_TILED) ? kModeTiled : kModeAuto;
   const int E = d.E;
   const int I = static_cast<int>(d.I);
+  const bool up = parts & kGemmUp, down = parts & kGemmDown;
   GemmArgs g1{p.Xe, w1, p.h, p.counts, p.offsets, E, static_cast<int>(d.H), I, mode};
   GemmArgs g2{p.h, w2, p.O, p.counts, p.offsets, E, I, static_cast<int>(d.H), mode};
+  hipError_t err;
 
   if (d.dtype == TR_F32) {
     const int64_t tiles1 = (cdiv(p.R_cap, F_BM) + E) * cdiv(I, F_BN);
     const int64_t tiles2 = (cdiv(p.R_cap, F_BM) + E) * cdiv(d.H, F_BN);
     const unsigned grid1 = static_cast<unsigned>(tiles1 < cus * 8 ? tiles1 : cus * 8);
     const unsigned grid2 = static_cast<unsigned>(tiles2 < cus * 8 ? tiles2 : cus * 8);
-    hipLaunchKernelGGL(gemm_f32<true>, dim3(grid1), dim3(kThreads), 0, st, g1, I);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(gemm_f32<false>, dim3(grid2), dim3(kThreads), 0, st, g2, I);
-    return hipGetLastError();
+    if (up) {
+      hipLaunchKernelGGL(gemm_f32<true>, dim3(grid1), dim3(kThreads), 0, st, g1, I);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (down) {
+      hipLaunchKernelGGL(gemm_f32<false>, dim3(grid2), dim3(kThreads), 0, st, g2, I);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
   }
 
   // tiled: persistent, one block per CU; stream: persistent, 8 blocks per CU
@@ -503,20 +510,19 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, hi
   const int64_t u1 = static_cast<int64_t>(E) * cdiv(I, 8), u2 = static_cast<int64_t>(E) * cdiv(d.H, 16);
   const unsigned gs1 = static_cast<unsigned>(u1 < cus * 8 ? u1 : cus * 8);
   const unsigned gs2 = static_cast<unsigned>(u2 < cus * 8 ? u2 : cus * 8);
-  hipError_t err;
-  if (mode != kModeStream) {
+  if (up && mode != kModeStream) {
     hipLaunchKernelGGL(gemm_tiled<true>, dim3(gt1), dim3(kThreads), 0, st, g1, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (mode != kModeTiled) {
+  if (up && mode != kModeTiled) {
     hipLaunchKernelGGL(gemm_stream<true>, dim3(gs1), dim3(kThreads), 0, st, g1, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (mode != kModeStream) {
+  if (down && mode != kModeStream) {
     hipLaunchKernelGGL(gemm_tiled<false>, dim3(gt2), dim3(kThreads), 0, st, g2, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (mode != kModeTiled) {
+  if (down && mode != kModeTiled) {
     hipLaunchKernelGGL(gemm_stream<false>, dim3(gs2), dim3(kThreads), 0, st, g2, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }

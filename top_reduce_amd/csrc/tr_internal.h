@@ -16,7 +16,10 @@ constexpr int kStreamMaxRows = 32;
 hipError_t route_scan(const tr_moe_plan& p, const void* idx, hipStream_t st);
 void route_scan_geometry(int64_t T, int K, int* blocks, int* rows_per_block);
 hipError_t expand(const tr_moe_plan& p, const void* x, hipStream_t st);
-hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, hipStream_t st);
+enum { kGemmUp = 1, kGemmDown = 2 };
+// parts: kGemmUp (Xe -> h, SwiGLU), kGemmDown (h -> O), or both.
+hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, int parts,
+                        hipStream_t st);
 hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const float* w, void* y,
                           hipStream_t st);
 
