@@ -27,6 +27,9 @@
  *    Calls are graph-capturable except moe_plan_stats.
  *  - Arrays are dense and row-major. x, y, W1, W2 and the expert buffers are
  *    all of one element type, desc->dtype.
+ *  - Shapes: bf16 needs H a multiple of 256 and I a multiple of 128 (whole
+ *    GEMM tiles along the output columns); fp32 needs H a multiple of 8.
+ *    Other shapes return TR_EUNSUPPORTED.
  *  - Errors: a non-zero tr_status and a message in moe_last_error(). Argument
  *    checks happen on the host before anything is enqueued. Nothing aborts.
  *  - Ids outside [expert_begin, expert_begin + E), -1 included, are routes to
@@ -93,8 +96,8 @@ typedef struct tr_moe_plan {
     int32_t* row_k;        /* [R_cap] slot of expanded row r (r < R) */
     int32_t* stats;        /* [4] R, rows with >= 1 local route, ignored slots, empty experts */
     int32_t* scan_tmp;     /* route-scan block partials */
-    void* Xe;              /* [R_cap, H] expanded rows (expert-contiguous) */
-    void* h;               /* [R_cap, I] silu(gate) * up */
+    void* Xe;              /* [R_cap + 256, H] expanded rows (expert-contiguous) */
+    void* h;               /* [R_cap + 256, I] silu(gate) * up */
     void* O;               /* [R_cap, H] expert outputs */
     int32_t scan_blocks;
     int32_t scan_rows_per_block;

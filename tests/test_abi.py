@@ -77,9 +77,11 @@ def test_workspace_size_and_desc_checks():
         args.update(kw)
         assert _ws(tr.make_desc(**args)) == 0, kw
         assert lib.moe_last_error()
-    # bf16 needs H, I multiples of 64; fp32 needs H multiple of 8
-    assert _ws(tr.make_desc(T=8, K=2, E=4, H=100, I=64)) == 0
-    assert b"multiples of 64" in lib.moe_last_error()
+    # bf16 needs H a multiple of 256 and I of 128; fp32 needs H a multiple of 8
+    assert _ws(tr.make_desc(T=8, K=2, E=4, H=100, I=128)) == 0
+    assert b"multiple of 256" in lib.moe_last_error()
+    assert _ws(tr.make_desc(T=8, K=2, E=4, H=512, I=64)) == 0
+    assert _ws(tr.make_desc(T=8, K=2, E=4, H=512, I=128)) > 0
     assert _ws(tr.make_desc(T=8, K=2, E=4, H=104, I=72, dtype=torch.float32)) > 0
     d = tr.make_desc(T=8, K=2, E=4, H=64, I=64, flags=3)
     assert _ws(d) == 0

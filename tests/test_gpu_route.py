@@ -15,7 +15,7 @@ from tests._gpu import say
 pytestmark = pytest.mark.gpu
 
 
-def _check(idx_np, E, eb=0, idx_dtype=torch.int64, H=64, I=64):
+def _check(idx_np, E, eb=0, idx_dtype=torch.int64, H=256, I=128):
     T, K = idx_np.shape
     say(f"route T={T} K={K} E={E} eb={eb} idx={idx_dtype}")
     idx = torch.from_numpy(np.ascontiguousarray(idx_np)).to(idx_dtype).cuda()
@@ -65,8 +65,8 @@ def test_route_edge_cases():
 def test_route_deterministic():
     wl = gen.make_workload("c5")
     idx = torch.from_numpy(wl.idx).cuda()
-    a = tr.plan(idx, E=wl.E, H=64, I=64).views()
-    b = tr.plan(idx, E=wl.E, H=64, I=64).views()
+    a = tr.plan(idx, E=wl.E, H=256, I=128).views()
+    b = tr.plan(idx, E=wl.E, H=256, I=128).views()
     R = int(a["stats"][0])
     for f in ("counts", "offsets", "row_map", "stats"):
         assert torch.equal(a[f], b[f]), f

@@ -43,14 +43,16 @@ tr_status check_desc(const tr_moe_desc* d) {
   const int32_t known = TR_FLAG_GEMM_FORCE_TILED | TR_FLAG_GEMM_FORCE_STREAM;
   if (d->flags & ~known) return fail(TR_EINVAL, "unknown flags 0x%x", d->flags);
   if ((d->flags & known) == known) return fail(TR_EINVAL, "both GEMM force flags set");
-  if (d->H > (1 << 24) || d->I > (1 << 24)) return fail(TR_EUNSUPPORTED, "H and I must be <= 2^24");
+  // GEMM tiles address one expert's weights with 32-bit element offsets.
+  if (d->H > (1 << 22) || d->I > (1 << 22) || 2 * d->H * d->I >= (int64_t(1) << 31))
+    return fail(TR_EUNSUPPORTED, "H, I must be <= 2^22 and 2*H*I < 2^31");
   if (d->T > (int64_t(1) << 31) / d->K) return fail(TR_EUNSUPPORTED, "T*K must be < 2^31");
   if (d->expert_begin > (int64_t(1) << 62) || d->expert_begin < -(int64_t(1) << 62))
     return fail(TR_EINVAL, "expert_begin out of range");
   if (d->dtype == TR_BF16) {
-    if (d->H % 64 || d->I % 64)
-      return fail(TR_EUNSUPPORTED, "bf16 needs H and I multiples of 64 (got H=%lld I=%lld)",
-                  (long long)d->H, (long long)d->I);
+    if (d->H % tr::kColMultiple || d->I % (tr::kColMultiple / 2))
+      return fail(TR_EUNSUPPORTED, "bf16 needs H a multiple of %d and I of %d (got H=%lld I=%lld)",
+                  tr::kColMultiple, tr::kColMultiple / 2, (long long)d->H, (long long)d->I);
   } else {
     if (d->H % 8) return fail(TR_EUNSUPPORTED, "fp32 needs H a multiple of 8 (got %lld)", (long long)d->H);
   }
@@ -78,8 +80,8 @@ Layout layout(const tr_moe_desc& d) {
   L.row_src = take(sizeof(int32_t) * L.R_cap);
   L.row_k = take(sizeof(int32_t) * L.R_cap);
   L.scan_tmp = take(sizeof(int32_t) * static_cast<size_t>(L.blocks) * (d.E + 2));
-  L.Xe = take(es * L.R_cap * d.H);
-  L.h = take(es * L.R_cap * d.I);
+  L.Xe = take(es * (L.R_cap + tr::kRowPad) * d.H);
+  L.h = take(es * (L.R_cap + tr::kRowPad) * d.I);
   L.O = take(es * L.R_cap * d.H);
   L.total = o;
   return L;

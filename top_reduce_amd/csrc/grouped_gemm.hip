@@ -42,7 +42,7 @@ __device__ __forceinline__ bool goes_to_stream(int c, int mode) {
 }
 
 struct GemmArgs {
-  const void* A;        // [R_cap, Kd] rows (Xe for GEMM1, h for GEMM2)
+  const void* A;        // [a_rows, Kd] rows (Xe for GEMM1, h for GEMM2)
   const void* B;        // [E, Nb, Kd] weights (W1: Nb = 2I, W2: Nb = H)
   void* C;              // [R_cap, Nc] outputs (h: Nc = I, O: Nc = H)
   const int* counts;
@@ -51,6 +51,7 @@ struct GemmArgs {
   int Kd;               // reduction length
   int Nc;               // output columns
   int mode;
+  int64_t a_rows;       // rows allocated in A: R_cap + BM
 };
 
 // Builds in LDS the exclusive prefix of `units(e)` over experts; returns the
@@ -99,29 +100,135 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // Tiled MFMA kernel (bf16)
 // --------------------------------------------------------------------------
 constexpr int BM = 256, BN = 256, BK = 64;
-constexpr int kChunksPerRow = BK / 8;               // 16-byte chunks per tile row
-constexpr int kTileChunks = (BM + BN) * kChunksPerRow;  // per stage, 16-byte units
-constexpr int kLoadsPerThread = BM * kChunksPerRow / kThreads;  // 8 for A, 8 for B
-constexpr int kGroupM = 4;
+static_assert(BM <= kRowPad, "A buffers must carry BM spare rows");
+static_assert(BN == kColMultiple, "the H granularity must match the tile");
+constexpr int kCpr = BK / 8;                          // 16-byte chunks per tile row (8)
+constexpr int kRegion = BM * kCpr;                    // 16-byte units per operand per stage
+constexpr int kStageUnits = 2 * kRegion;              // A then B: 64 KiB per stage
+constexpr int kWavesT = kThreads / kWave;             // 4
+constexpr int kDmaPerWave = kStageUnits / kWave / kWavesT;  // 16 x 1 KiB per wave per stage
+constexpr int kSub = BK / 16;                         // MFMA k-steps per stage (4)
+[[maybe_unused]] constexpr int kGroupM = 4;
+// Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle).
+[[maybe_unused]] constexpr int kBufferFlags = 0x00020000;
+// s_waitcnt immediates (gfx9 encoding; fields not waited on are at maximum):
+// vmcnt(kDmaPerWave) = vmcnt(16), and vmcnt(0) + lgkmcnt(0).
+[[maybe_unused]] constexpr int kWaitVm16 = 0x4000 | 0x0F70;
+[[maybe_unused]] constexpr int kWaitVm0Lgkm0 = 0x0070;
+static_assert(kDmaPerWave == 16, "kWaitVm16 encodes vmcnt(16)");
+
+// Row r of a stage keeps its logical 16-byte chunk c at physical chunk
+// c ^ (r & 7): the 8 rows one LDS cycle serves hit 8 distinct bank groups.
+
+// Workgroup barrier that orders LDS accesses for the compiler only. It does
+// not wait for in-flight LDS DMA (callers wait with vmcnt first).
+[[maybe_unused]] __device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Two LDS stages as distinct objects: reads of one provably do not alias DMA
+// into the other, so the compiler adds no wait for in-flight DMA before them.
+__shared__ u32x4 g_stage0[kStageUnits];
+__shared__ u32x4 g_stage1[kStageUnits];
+
+template <int S>
+__device__ __forceinline__ u32x4* stage_ptr() { return S == 0 ? g_stage0 : g_stage1; }
+[[maybe_unused]] __device__ __forceinline__ u32x4* stage_ptr_rt(int s) {
+  return s == 0 ? g_stage0 : g_stage1;
+}
+
+// The buffer-resource type exists only in the device compilation pass, so
+// the per-tile context and the pipeline helpers are device-pass only.
+#if defined(__HIP_DEVICE_COMPILE__)
+template <bool kSwiglu>
+struct TileCtx {
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t voff;                 // this lane's byte offset for DMA 0 of a stage
+  uint32_t dma_stride;           // bytes between the rows of DMA j and j + 1
+  int dma_dst;
+  int a_frag, b_frag;
+  int frag_ch[kSub];
+  bf16x8 fa[2][4], fb[2][4];     // fragments of two MFMA k-steps
+  floatx16 acc[4][4];
+};
+
+// Stage S <- k-tile kt: 16 DMA of 1 KiB (8 rows x 128 B) per wave.
+template <int S, bool kSwiglu>
+__device__ __forceinline__ void issue_stage(TileCtx<kSwiglu>& c, int kt) {
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        c.rsrc, (lds_void*)(stage_ptr<S>() + c.dma_dst + j * 8 * kCpr), 16, c.voff,
+        kt * BK * 2 + j * c.dma_stride, 0, 0);
+}
+
+// Fragments of MFMA k-step `sub` of stage S into register set P.
+template <int S, int P, bool kSwiglu>
+__device__ __forceinline__ void read_frags(TileCtx<kSwiglu>& c, int sub) {
+  const u32x4* base = stage_ptr<S>();
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c.fa[P][i] = __builtin_bit_cast(bf16x8, base[c.a_frag + i * 32 * kCpr + c.frag_ch[sub]]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rb = kSwiglu ? (j < 2 ? j * 32 : 128 + (j - 2) * 32) : j * 32;
+    c.fb[P][j] = __builtin_bit_cast(bf16x8, base[c.b_frag + rb * kCpr + c.frag_ch[sub]]);
+  }
+}
+
+template <int P, bool kSwiglu>
+__device__ __forceinline__ void mma(TileCtx<kSwiglu>& c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      c.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.fa[P][i], c.fb[P][j], c.acc[i][j], 0, 0, 0);
+}
+
+// One k-tile held in stage S, with its first k-step's fragments already in
+// register set 0. The DMA of the next k-tile into the other stage is in
+// flight. Fragment reads run one MFMA k-step ahead; before the last k-step's
+// MFMAs the wave waits for the next k-tile's DMA and drains its LDS reads,
+// all waves meet, the next k-tile's first fragments are read and stage S is
+// refilled with k-tile kt + 2, so the barrier hides behind 16 MFMAs.
+template <int S, bool kSwiglu>
+__device__ __forceinline__ void ring_step(TileCtx<kSwiglu>& c, int kt, int nk) {
+  read_frags<S, 1>(c, 1);
+  mma<0>(c);
+  read_frags<S, 0>(c, 2);
+  mma<1>(c);
+  read_frags<S, 1>(c, 3);
+  mma<0>(c);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);   // k-tile kt+1 landed; stage S read
+  lds_barrier();
+  read_frags<1 - S, 0>(c, 0);
+  issue_stage<S>(c, min(kt + 2, nk - 1));
+  mma<1>(c);
+}
+#endif  // __HIP_DEVICE_COMPILE__
 
 template <bool kSwiglu>
 __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
-  __shared__ u32x4 lds[2][kTileChunks];
+#if defined(__HIP_DEVICE_COMPILE__)
   __shared__ int pre[kMaxE + 1];
-  __shared__ int tmp[kThreads / kWave];
+  __shared__ int tmp[kWavesT];
 
   const int mode = a.mode;
   const int total_m = expert_prefix(a.counts, a.E, [mode](int c) {
     return (c > 0 && !goes_to_stream(c, mode)) ? (c + BM - 1) / BM : 0;
   }, pre, tmp);
-  const int n_cols_per_tile = kSwiglu ? BN / 2 : BN;
-  const int NT = (a.Nc + n_cols_per_tile - 1) / n_cols_per_tile;
+  constexpr int kOutCols = kSwiglu ? BN / 2 : BN;   // output columns per tile
+  const int NT = (a.Nc + kOutCols - 1) / kOutCols;
   const int total = total_m * NT;
   if (total == 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int Kd = a.Kd;
   const int64_t Nb = kSwiglu ? 2 * static_cast<int64_t>(I) : a.Nc;
@@ -135,11 +242,28 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   int pos = blockIdx.x;
   if ((G & 7) == 0) pos = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
 
-  // Per-thread load geometry: chunk column is fixed, rows step by 32.
-  const int ld_row = tid >> 3;   // + 32 * j
-  const int ld_ch = tid & 7;
-
   for (int L = pos; L < total; L += G) {
+    // Lane geometry is recomputed per tile from an opaque copy of the lane id,
+    // so its registers are not held across the epilogue.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    TileCtx<kSwiglu> c;
+    // DMA geometry: waves 0-1 fill the A region, waves 2-3 the B region. DMA j
+    // of a wave writes 1 KiB = 8 rows x 8 chunks: lane -> (row lane / 8,
+    // physical chunk lane % 8), so the lane fetches logical chunk
+    // (lane % 8) ^ (row % 8) = (lane % 8) ^ (lane / 8).
+    const int dma_b = wave >> 1;
+    const int dma_row0 = (wave & 1) * (BM / 2) + (ln >> 3);     // + 8 j
+    const int dma_chunk = (ln & 7) ^ (ln >> 3);
+    c.dma_dst = dma_b * kRegion + (wave & 1) * (BM / 2) * kCpr;
+    // Fragments: lane reads row (lane & 31) of a 32-row block at logical
+    // chunk 2 s + lane / 32 in MFMA k-step s.
+#pragma unroll
+    for (int s = 0; s < kSub; ++s)
+      c.frag_ch[s] = (ln & 31) * kCpr + ((2 * s + (ln >> 5)) ^ (ln & 7));
+    c.a_frag = wm * 128 * kCpr;
+    c.b_frag = kRegion + (kSwiglu ? wn * 64 : wn * 128) * kCpr;
+
     // tile order: groups of kGroupM m-tiles x all n-tiles, m fastest
     const int group = L / (kGroupM * NT);
     const int first = group * kGroupM;
@@ -147,119 +271,112 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     const int within = L - group * kGroupM * NT;
     const int gm = first + within % gsz;
     const int nt = within / gsz;
-    const int e = find_expert(pre, a.E, gm);
-    const int mt = gm - pre[e];
-    const int cnt = a.counts[e];
-    const int row0 = a.offsets[e] + mt * BM;
+    // tile parameters are block-uniform; say so, so that the buffer
+    // resources below live in scalar registers
+    const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, a.E, gm));
+    const int mt = __builtin_amdgcn_readfirstlane(gm - pre[e]);
+    const int cnt = __builtin_amdgcn_readfirstlane(a.counts[e]);
+    const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + mt * BM;
     const int rows_valid = min(BM, cnt - mt * BM);
-    const int n0 = nt * n_cols_per_tile;
+    const int n0 = nt * kOutCols;
 
-    // global offsets (elements) of this thread's 8 A rows and 8 B rows
-    int64_t aoff[kLoadsPerThread], boff[kLoadsPerThread];
+    // Buffer resources over this tile's A rows and expert e's weights. Every
+    // DMA address is in bounds by construction: the A buffers (Xe, h) carry
+    // BM spare rows past R_cap, so a tile may read BM rows from any segment
+    // start (rows past the segment only feed discarded outputs), and the
+    // weight rows of a tile never pass the expert's 2I (or H) rows because I
+    // is a multiple of BN / 2 and H of BN. Row offsets go in the scalar
+    // offset, so a lane keeps a single offset register.
+    const uint64_t a_left = (static_cast<uint64_t>(a.a_rows) - row0) * Kd * 2;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Ab + static_cast<int64_t>(row0) * Kd), 0,
+        static_cast<int>(a_left < 0xffffffffull ? a_left : 0xffffffffull), kBufferFlags);
+    const uint64_t b_size = static_cast<uint64_t>(Nb) * Kd * 2;
+    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(Bb + static_cast<int64_t>(e) * Nb * Kd), 0,
+        static_cast<int>(b_size < 0xffffffffull ? b_size : 0xffffffffull), kBufferFlags);
+    c.rsrc = dma_b ? rB : rA;
+    int row = dma_row0;                          // A: tile row of DMA 0
+    if (dma_b) {
+      if (kSwiglu) row = (wave & 1) ? I + n0 + (ln >> 3) : n0 + (ln >> 3);   // gate | up
+      else row = n0 + dma_row0;
+    }
+    c.voff = (static_cast<uint32_t>(row) * Kd + dma_chunk * 8) * 2;
+    c.dma_stride = 8u * Kd * 2;
+    // Accumulators start at zero through an MFMA with zero operands: the
+    // result lands in accumulation registers directly, instead of 256 zeros
+    // built in ordinary vector registers first.
+    {
+      bf16x8 zf;
+      int zero = 0;
+      asm volatile("" : "+v"(zero));
 #pragma unroll
-    for (int j = 0; j < kLoadsPerThread; ++j) {
-      const int r = ld_row + 32 * j;
-      const int rr = min(r, rows_valid - 1);
-      aoff[j] = static_cast<int64_t>(row0 + rr) * Kd + ld_ch * 8;
-      int64_t brow;
-      if (kSwiglu) {
-        const int half = r >> 7;            // 0: gate rows, 1: up rows
-        const int c = min(n0 + (r & 127), I - 1);
-        brow = half ? I + c : c;
-      } else {
-        brow = min(n0 + r, a.Nc - 1);
-      }
-      boff[j] = (static_cast<int64_t>(e) * Nb + brow) * Kd + ld_ch * 8;
+      for (int q = 0; q < 8; ++q) zf[q] = __builtin_bit_cast(__bf16, static_cast<uint16_t>(zero));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          c.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf, zf, floatx16{}, 0, 0, 0);
     }
 
-    floatx16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-    u32x4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-    auto gload = [&](int k0) {
-#pragma unroll
-      for (int j = 0; j < kLoadsPerThread; ++j) {
-        ra[j] = *reinterpret_cast<const u32x4*>(Ab + aoff[j] + k0);
-        rb[j] = *reinterpret_cast<const u32x4*>(Bb + boff[j] + k0);
-      }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-      for (int j = 0; j < kLoadsPerThread; ++j) {
-        const int r = ld_row + 32 * j;
-        const int sw = ld_ch ^ (r & 7);
-        lds[buf][r * kChunksPerRow + sw] = ra[j];
-        lds[buf][(BM + r) * kChunksPerRow + sw] = rb[j];
-      }
-    };
-
+    // Two LDS stages: k-tile kt+1 streams in while k-tile kt is multiplied.
+    // Tiles past the end re-read the last one (uniform control flow); their
+    // data is never used.
     const int nk = Kd / BK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-      for (int s = 0; s < BK / 16; ++s) {
-        const int ch = (2 * s + (lane >> 5)) ^ (lane & 7);
-        bf16x8 fa[4], fb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = wm * 128 + i * 32 + (lane & 31);
-          const u32x4 t = lds[cur][r * kChunksPerRow + ch];
-          fa[i] = __builtin_bit_cast(bf16x8, t);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          int r;
-          if (kSwiglu) r = (j < 2 ? wn * 64 + j * 32 : 128 + wn * 64 + (j - 2) * 32) + (lane & 31);
-          else r = wn * 128 + j * 32 + (lane & 31);
-          const u32x4 t = lds[cur][(BM + r) * kChunksPerRow + ch];
-          fb[j] = __builtin_bit_cast(bf16x8, t);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < nk) sstore(cur ^ 1);
-      __syncthreads();
+    issue_stage<0>(c, 0);
+    issue_stage<1>(c, min(1, nk - 1));
+    __builtin_amdgcn_s_waitcnt(kWaitVm16);      // k-tile 0 (own DMA)
+    lds_barrier();
+    read_frags<0, 0>(c, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+      ring_step<0>(c, kt, nk);
+      if (kt + 1 < nk) ring_step<1>(c, kt + 1, nk);
     }
+    __builtin_amdgcn_s_waitcnt(0);              // drain the ring before reuse
+    __syncthreads();
 
-    // epilogue: lane owns column (lane & 31) of each 32x32 block and rows
-    // 8*(v/4) + 4*(lane/32) + (v%4)
+    // Epilogue: stage the bf16 tile in LDS row-major [BM][kOutCols] (rows
+    // split evenly over the two stage buffers), then write whole 16-byte
+    // chunks of rows. Lane owns column (lane & 31) of each 32x32 block and
+    // rows 8 (v / 4) + 4 (lane / 32) + (v % 4).
+    constexpr int kRowsPerStage = kStageUnits * 8 / kOutCols;   // 128 or 256
+    constexpr int kBlocksPerStage = kRowsPerStage / 32;          // 32-row blocks
+    // This wave's rows wm*128 + [0, 128) sit in buffer wm*128 / kRowsPerStage.
+    const int lane_off = 4 * (ln >> 5) * kOutCols + (kSwiglu ? wn * 64 : wn * 128) + (ln & 31);
+    uint16_t* ob = reinterpret_cast<uint16_t*>(stage_ptr_rt((wm * 128) / kRowsPerStage)) +
+                   ((wm * 128) % kRowsPerStage) * kOutCols + lane_off;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      uint16_t* base = ob + i * 32 * kOutCols;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (r >= rows_valid) continue;
-        const int64_t orow = static_cast<int64_t>(row0 + r) * a.Nc;
+        uint16_t* orow = base + (8 * (v >> 2) + (v & 3)) * kOutCols;
         if (kSwiglu) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-            if (col < a.Nc)
-              Cb[orow + col] = static_cast<uint16_t>(
-                  f32_to_bf16_bits(silu_mul(acc[i][j][v], acc[i][j + 2][v])));
-          }
+          for (int j = 0; j < 2; ++j)
+            orow[j * 32] = static_cast<uint16_t>(
+                f32_to_bf16_bits(silu_mul(c.acc[i][j][v], c.acc[i][j + 2][v])));
         } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 128 + j * 32 + (lane & 31);
-            if (col < a.Nc) Cb[orow + col] = static_cast<uint16_t>(f32_to_bf16_bits(acc[i][j][v]));
-          }
+          for (int j = 0; j < 4; ++j)
+            orow[j * 32] = static_cast<uint16_t>(f32_to_bf16_bits(c.acc[i][j][v]));
         }
+        // convert a few accumulators at a time: bounded register pressure
+        if ((v & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     }
+    (void)kBlocksPerStage;
+    __syncthreads();
+    constexpr int kOutChunks = kOutCols / 8;   // 16-byte chunks per output row
+    for (int q = tid; q < BM * kOutChunks; q += kThreads) {
+      const int r = q / kOutChunks, ch = q % kOutChunks, col = n0 + ch * 8;
+      if (r < rows_valid && col < a.Nc)
+        *reinterpret_cast<u32x4*>(Cb + static_cast<int64_t>(row0 + r) * a.Nc + col) =
+            stage_ptr_rt(r / kRowsPerStage)[(r % kRowsPerStage) * kOutChunks + ch];
+    }
+    __syncthreads();
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
 // --------------------------------------------------------------------------
@@ -482,8 +599,9 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   const int E = d.E;
   const int I = static_cast<int>(d.I);
   const bool up = parts & kGemmUp, down = parts & kGemmDown;
-  GemmArgs g1{p.Xe, w1, p.h, p.counts, p.offsets, E, static_cast<int>(d.H), I, mode};
-  GemmArgs g2{p.h, w2, p.O, p.counts, p.offsets, E, I, static_cast<int>(d.H), mode};
+  const int64_t a_rows = p.R_cap + kRowPad;
+  GemmArgs g1{p.Xe, w1, p.h, p.counts, p.offsets, E, static_cast<int>(d.H), I, mode, a_rows};
+  GemmArgs g2{p.h, w2, p.O, p.counts, p.offsets, E, I, static_cast<int>(d.H), mode, a_rows};
   hipError_t err;
 
   if (d.dtype == TR_F32) {

@@ -93,12 +93,25 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rpb;
   const int64_t r1 = r0 + rpb < T ? r0 + rpb : T;
 
-  for (int i = tid; i < kWaves * (E + 1); i += kThreads) wcnt[i] = 0;
+  int* prior = wcnt;                    // [E] phase 1 only; wcnt is zeroed after
+  for (int i = tid; i < E + 2; i += kThreads) cnt[i] = 0;
+  for (int i = tid; i < E; i += kThreads) prior[i] = 0;
   if (tid < 4) misc[tid] = 0;
+  __syncthreads();
   if (kSelf) {
-    for (int i = tid; i < E + 2; i += kThreads) cnt[i] = 0;
-    __syncthreads();
     count_rows(idx, r0, r1, K, eb, E, cnt);
+  } else {
+    // totals and this block's prior counts from every block's partials; all
+    // threads share the (block, expert) grid so the loads are independent
+    const int n = nblocks * E;
+    for (int i = tid; i < n; i += kThreads) {
+      const int b = i / E, e = i - b * E;
+      const int c = hist[b * (E + 2) + e];
+      if (c) {
+        atomicAdd(&cnt[e], c);
+        if (b < static_cast<int>(blockIdx.x)) atomicAdd(&prior[e], c);
+      }
+    }
   }
   __syncthreads();
 
@@ -112,18 +125,13 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     pri[j] = 0;
     const int e = tid * per + j;
     if (j < per && e < E) {
-      if (kSelf) {
-        tot[j] = cnt[e];
-      } else {
-        for (int b = 0; b < nblocks; ++b) {
-          const int c = hist[b * (E + 2) + e];
-          tot[j] += c;
-          if (b < static_cast<int>(blockIdx.x)) pri[j] += c;
-        }
-      }
+      tot[j] = cnt[e];
+      pri[j] = kSelf ? 0 : prior[e];
       tsum += tot[j];
     }
   }
+  __syncthreads();                      // prior[] read; wcnt becomes per-wave counts
+  for (int i = tid; i < kWaves * (E + 1); i += kThreads) wcnt[i] = 0;
   int R = 0;
   int off = block_exclusive_scan<kThreads>(tsum, tmp, &R);
 #pragma unroll

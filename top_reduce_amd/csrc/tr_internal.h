@@ -12,6 +12,11 @@ constexpr int kMaxK = 32;
 constexpr int kMaxE = 1024;
 // Experts with at most this many routes go to the weight-streaming GEMM.
 constexpr int kStreamMaxRows = 32;
+// Spare rows after R_cap in the expanded (Xe) and intermediate (h) buffers,
+// so GEMM tiles may read a full tile of rows from any segment start.
+constexpr int kRowPad = 256;
+// bf16 shapes: H a multiple of kColMultiple, I of kColMultiple / 2.
+constexpr int kColMultiple = 256;
 
 hipError_t route_scan(const tr_moe_plan& p, const void* idx, hipStream_t st);
 void route_scan_geometry(int64_t T, int K, int* blocks, int* rows_per_block);
