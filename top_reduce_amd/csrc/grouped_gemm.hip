@@ -114,8 +114,14 @@ constexpr int kSub = BK / 16;                         // MFMA k-steps per stage 
 // s_waitcnt immediates (gfx9 encoding; fields not waited on are at maximum):
 // vmcnt(kDmaPerWave) = vmcnt(16), and vmcnt(0) + lgkmcnt(0).
 [[maybe_unused]] constexpr int kWaitVm16 = 0x4000 | 0x0F70;
-[[maybe_unused]] constexpr int kWaitVm0Lgkm0 = 0x0070;
+[[maybe_unused]] constexpr int kWaitVm2Lgkm0 = 0x0072;
 static_assert(kDmaPerWave == 16, "kWaitVm16 encodes vmcnt(16)");
+// L2 prefetch: k-tile kt + 2 + kPrefetchAhead is touched (one dword per
+// 128-byte line, all BM + BN rows) when k-tile kt + 2 is requested, so the
+// real DMA later finds its lines in L2. Two 64-line DMAs per wave.
+constexpr int kPrefetchAhead = 2;
+constexpr int kPrefetchPerWave = 2;
+static_assert(kPrefetchPerWave == 2, "kWaitVm2Lgkm0 encodes vmcnt(2)");
 
 // Row r of a stage keeps its logical 16-byte chunk c at physical chunk
 // c ^ (r & 7): the 8 rows one LDS cycle serves hit 8 distinct bank groups.
@@ -134,6 +140,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 // into the other, so the compiler adds no wait for in-flight DMA before them.
 __shared__ u32x4 g_stage0[kStageUnits];
 __shared__ u32x4 g_stage1[kStageUnits];
+// Destination of the L2-prefetch DMAs: written, never read.
+__shared__ uint32_t g_prefetch_sink[kWave];
 
 template <int S>
 __device__ __forceinline__ u32x4* stage_ptr() { return S == 0 ? g_stage0 : g_stage1; }
@@ -149,6 +157,8 @@ struct TileCtx {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff;                 // this lane's byte offset for DMA 0 of a stage
   uint32_t dma_stride;           // bytes between the rows of DMA j and j + 1
+  uint32_t pf_off;               // this lane's row (prefetch DMA 0), bytes
+  uint32_t pf_stride;            // bytes between the rows of prefetch DMA 0 and 1
   int dma_dst;
   int a_frag, b_frag;
   int frag_ch[kSub];
@@ -164,6 +174,15 @@ __device__ __forceinline__ void issue_stage(TileCtx<kSwiglu>& c, int kt) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         c.rsrc, (lds_void*)(stage_ptr<S>() + c.dma_dst + j * 8 * kCpr), 16, c.voff,
         kt * BK * 2 + j * c.dma_stride, 0, 0);
+}
+
+// Pull the lines of k-tile kt into L2: lane -> one row, one dword per line.
+template <bool kSwiglu>
+__device__ __forceinline__ void prefetch_l2(TileCtx<kSwiglu>& c, int kt) {
+#pragma unroll
+  for (int q = 0; q < kPrefetchPerWave; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, (lds_void*)g_prefetch_sink, 4, c.pf_off,
+                                             kt * BK * 2 + q * c.pf_stride, 0, 0);
 }
 
 // Fragments of MFMA k-step `sub` of stage S into register set P.
@@ -195,19 +214,33 @@ __device__ __forceinline__ void mma(TileCtx<kSwiglu>& c) {
 // MFMAs the wave waits for the next k-tile's DMA and drains its LDS reads,
 // all waves meet, the next k-tile's first fragments are read and stage S is
 // refilled with k-tile kt + 2, so the barrier hides behind 16 MFMAs.
+// The scheduling barriers pin this order: the compiler would otherwise sink
+// each fragment read next to its first use and wait on it, exposing LDS
+// latency every few MFMAs.
 template <int S, bool kSwiglu>
 __device__ __forceinline__ void ring_step(TileCtx<kSwiglu>& c, int kt, int nk) {
   read_frags<S, 1>(c, 1);
+  __builtin_amdgcn_sched_barrier(0);
   mma<0>(c);
+  __builtin_amdgcn_sched_barrier(0);
   read_frags<S, 0>(c, 2);
+  __builtin_amdgcn_sched_barrier(0);
   mma<1>(c);
+  __builtin_amdgcn_sched_barrier(0);
   read_frags<S, 1>(c, 3);
+  __builtin_amdgcn_sched_barrier(0);
   mma<0>(c);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);   // k-tile kt+1 landed; stage S read
+  __builtin_amdgcn_sched_barrier(0);
+  // k-tile kt+1 landed (only its prefetch may still be in flight); stage S
+  // fully read by this wave
+  __builtin_amdgcn_s_waitcnt(kWaitVm2Lgkm0);
   lds_barrier();
   read_frags<1 - S, 0>(c, 0);
   issue_stage<S>(c, min(kt + 2, nk - 1));
+  prefetch_l2(c, min(kt + 2 + kPrefetchAhead, nk - 1));
+  __builtin_amdgcn_sched_barrier(0);
   mma<1>(c);
+  __builtin_amdgcn_sched_barrier(0);
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
@@ -303,6 +336,14 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     }
     c.voff = (static_cast<uint32_t>(row) * Kd + dma_chunk * 8) * 2;
     c.dma_stride = 8u * Kd * 2;
+    // prefetch rows: this wave's 128 rows of its operand, 64 per DMA
+    int pf_row = (wave & 1) * (BM / 2) + ln;                       // A tile row
+    if (dma_b) {
+      if (kSwiglu) pf_row = (wave & 1) ? I + n0 + ln : n0 + ln;   // gate | up
+      else pf_row = n0 + pf_row;
+    }
+    c.pf_off = static_cast<uint32_t>(pf_row) * Kd * 2;
+    c.pf_stride = static_cast<uint32_t>(kWave) * Kd * 2;
     // Accumulators start at zero through an MFMA with zero operands: the
     // result lands in accumulation registers directly, instead of 256 zeros
     // built in ordinary vector registers first.
@@ -326,6 +367,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     issue_stage<0>(c, 0);
     issue_stage<1>(c, min(1, nk - 1));
     __builtin_amdgcn_s_waitcnt(kWaitVm16);      // k-tile 0 (own DMA)
+    prefetch_l2(c, min(2, nk - 1));
+    prefetch_l2(c, min(3, nk - 1));
     lds_barrier();
     read_frags<0, 0>(c, 0);
     for (int kt = 0; kt < nk; kt += 2) {
