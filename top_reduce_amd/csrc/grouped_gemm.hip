@@ -107,21 +107,16 @@ constexpr int kRegion = BM * kCpr;                    // 16-byte units per opera
 constexpr int kStageUnits = 2 * kRegion;              // A then B: 64 KiB per stage
 constexpr int kWavesT = kThreads / kWave;             // 4
 constexpr int kDmaPerWave = kStageUnits / kWave / kWavesT;  // 16 x 1 KiB per wave per stage
-constexpr int kSub = BK / 16;                         // MFMA k-steps per stage (4)
-[[maybe_unused]] constexpr int kGroupM = 4;
+constexpr int kPfPerWave = 2;                         // L2-prefetch DMAs per wave per k-tile
+constexpr int kGroupM = 4;
 // Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle).
-[[maybe_unused]] constexpr int kBufferFlags = 0x00020000;
-// s_waitcnt immediates (gfx9 encoding; fields not waited on are at maximum):
-// vmcnt(kDmaPerWave) = vmcnt(16), and vmcnt(0) + lgkmcnt(0).
-[[maybe_unused]] constexpr int kWaitVm16 = 0x4000 | 0x0F70;
-[[maybe_unused]] constexpr int kWaitVm2Lgkm0 = 0x0072;
-static_assert(kDmaPerWave == 16, "kWaitVm16 encodes vmcnt(16)");
-// L2 prefetch: k-tile kt + 2 + kPrefetchAhead is touched (one dword per
-// 128-byte line, all BM + BN rows) when k-tile kt + 2 is requested, so the
-// real DMA later finds its lines in L2. Two 64-line DMAs per wave.
-constexpr int kPrefetchAhead = 2;
-constexpr int kPrefetchPerWave = 2;
-static_assert(kPrefetchPerWave == 2, "kWaitVm2Lgkm0 encodes vmcnt(2)");
+constexpr int kBufferFlags = 0x00020000;
+
+// s_waitcnt immediate (gfx9 encoding) for vmcnt(n) with lgkmcnt(0) or with
+// no lgkm wait; expcnt is never waited on.
+__host__ __device__ constexpr int waitcnt_vm(int n, bool lgkm0) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | ((lgkm0 ? 0 : 15) << 8);
+}
 
 // Row r of a stage keeps its logical 16-byte chunk c at physical chunk
 // c ^ (r & 7): the 8 rows one LDS cycle serves hit 8 distinct bank groups.
@@ -145,103 +140,175 @@ __shared__ uint32_t g_prefetch_sink[kWave];
 
 template <int S>
 __device__ __forceinline__ u32x4* stage_ptr() { return S == 0 ? g_stage0 : g_stage1; }
-[[maybe_unused]] __device__ __forceinline__ u32x4* stage_ptr_rt(int s) {
-  return s == 0 ? g_stage0 : g_stage1;
-}
 
 // The buffer-resource type exists only in the device compilation pass, so
-// the per-tile context and the pipeline helpers are device-pass only.
+// the tile state and the pipeline helpers are device-pass only.
 #if defined(__HIP_DEVICE_COMPILE__)
-template <bool kSwiglu>
-struct TileCtx {
+
+// Where one tile's operands come from: this wave's DMA source (A rows for
+// waves 0-1, weight rows for waves 2-3).
+struct TileSrc {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff;                 // this lane's byte offset for DMA 0 of a stage
-  uint32_t dma_stride;           // bytes between the rows of DMA j and j + 1
-  uint32_t pf_off;               // this lane's row (prefetch DMA 0), bytes
-  uint32_t pf_stride;            // bytes between the rows of prefetch DMA 0 and 1
-  int dma_dst;
-  int a_frag, b_frag;
-  int frag_ch[kSub];
-  bf16x8 fa[2][4], fb[2][4];     // fragments of two MFMA k-steps
-  floatx16 acc[4][4];
+  uint32_t voff;        // this lane's byte offset of DMA 0 of a k-tile
+  uint32_t stride;      // bytes between the 8-row groups of DMA j and j + 1
+  uint32_t pf_off;      // this lane's row for the L2 prefetch, bytes
+  uint32_t pf_stride;   // bytes between the two 64-row prefetch groups
 };
 
-// Stage S <- k-tile kt: 16 DMA of 1 KiB (8 rows x 128 B) per wave.
-template <int S, bool kSwiglu>
-__device__ __forceinline__ void issue_stage(TileCtx<kSwiglu>& c, int kt) {
+struct TileInfo {
+  int e, row0, rows_valid, n0;
+};
+
+// Lane geometry, fixed for the whole kernel.
+struct Geo {
+  int dma_dst;          // 16-byte unit of DMA 0 in a stage
+  int a_frag, b_frag;   // 16-byte unit of this wave's first A / B fragment row
+  int frag_ch[BK / 16]; // per MFMA k-step: row-in-block * 8 + swizzled chunk
+};
+
+struct Frags {
+  bf16x8 fa[2][4], fb[2][4];   // fragments of two MFMA k-steps
+  floatx16 acc[4][4];          // acc[i][j]: weight block j x row block i
+};
+
+// Stage S <- k-tile kt of `src`: 16 DMA of 1 KiB (8 rows x 128 B) per wave.
+template <int S>
+__device__ __forceinline__ void issue_stage(const Geo& g, const TileSrc& src, int kt) {
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        c.rsrc, (lds_void*)(stage_ptr<S>() + c.dma_dst + j * 8 * kCpr), 16, c.voff,
-        kt * BK * 2 + j * c.dma_stride, 0, 0);
+        src.rsrc, (lds_void*)(stage_ptr<S>() + g.dma_dst + j * 8 * kCpr), 16, src.voff,
+        kt * BK * 2 + j * src.stride, 0, 0);
 }
 
 // Pull the lines of k-tile kt into L2: lane -> one row, one dword per line.
-template <bool kSwiglu>
-__device__ __forceinline__ void prefetch_l2(TileCtx<kSwiglu>& c, int kt) {
+__device__ __forceinline__ void prefetch_l2(const TileSrc& src, int kt) {
 #pragma unroll
-  for (int q = 0; q < kPrefetchPerWave; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rsrc, (lds_void*)g_prefetch_sink, 4, c.pf_off,
-                                             kt * BK * 2 + q * c.pf_stride, 0, 0);
+  for (int q = 0; q < kPfPerWave; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsrc, (lds_void*)g_prefetch_sink, 4, src.pf_off,
+                                             kt * BK * 2 + q * src.pf_stride, 0, 0);
 }
 
 // Fragments of MFMA k-step `sub` of stage S into register set P.
 template <int S, int P, bool kSwiglu>
-__device__ __forceinline__ void read_frags(TileCtx<kSwiglu>& c, int sub) {
+__device__ __forceinline__ void read_frags(Frags& f, const Geo& g, int sub) {
   const u32x4* base = stage_ptr<S>();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    c.fa[P][i] = __builtin_bit_cast(bf16x8, base[c.a_frag + i * 32 * kCpr + c.frag_ch[sub]]);
+    f.fa[P][i] = __builtin_bit_cast(bf16x8, base[g.a_frag + i * 32 * kCpr + g.frag_ch[sub]]);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int rb = kSwiglu ? (j < 2 ? j * 32 : 128 + (j - 2) * 32) : j * 32;
-    c.fb[P][j] = __builtin_bit_cast(bf16x8, base[c.b_frag + rb * kCpr + c.frag_ch[sub]]);
+    f.fb[P][j] = __builtin_bit_cast(bf16x8, base[g.b_frag + rb * kCpr + g.frag_ch[sub]]);
   }
 }
 
-template <int P, bool kSwiglu>
-__device__ __forceinline__ void mma(TileCtx<kSwiglu>& c) {
+// The weight fragment is the MFMA's A operand: a lane then holds four
+// consecutive output columns of one row, ready for wide stores.
+template <int P>
+__device__ __forceinline__ void mma(Frags& f) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      c.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.fa[P][i], c.fb[P][j], c.acc[i][j], 0, 0, 0);
+      f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fb[P][j], f.fa[P][i], f.acc[i][j], 0, 0, 0);
 }
 
-// One k-tile held in stage S, with its first k-step's fragments already in
-// register set 0. The DMA of the next k-tile into the other stage is in
-// flight. Fragment reads run one MFMA k-step ahead; before the last k-step's
-// MFMAs the wave waits for the next k-tile's DMA and drains its LDS reads,
-// all waves meet, the next k-tile's first fragments are read and stage S is
-// refilled with k-tile kt + 2, so the barrier hides behind 16 MFMAs.
-// The scheduling barriers pin this order: the compiler would otherwise sink
-// each fragment read next to its first use and wait on it, exposing LDS
-// latency every few MFMAs.
+// One k-tile held in stage S, its first k-step's fragments already in
+// register set 0, the next k-tile's DMA in flight into the other stage.
+// Fragment reads run one MFMA k-step ahead (the scheduling barriers keep the
+// compiler from sinking each read next to its use). Before the last k-step's
+// MFMAs the wave waits for the next k-tile (kWait: vmcnt allowance, or -1
+// when there is none), drains its LDS reads, meets the other waves, reads the
+// next k-tile's first fragments and refills stage S from `dsrc` (if any),
+// so the barrier hides behind 16 MFMAs.
 template <int S, bool kSwiglu>
-__device__ __forceinline__ void ring_step(TileCtx<kSwiglu>& c, int kt, int nk) {
-  read_frags<S, 1>(c, 1);
+__device__ __forceinline__ void ring_step(Frags& f, const Geo& g, int wait_vm, bool issue,
+                                          const TileSrc& dsrc, int dkt, const TileSrc& psrc,
+                                          int pkt, bool pf) {
+  read_frags<S, 1, kSwiglu>(f, g, 1);
   __builtin_amdgcn_sched_barrier(0);
-  mma<0>(c);
+  mma<0>(f);
   __builtin_amdgcn_sched_barrier(0);
-  read_frags<S, 0>(c, 2);
+  read_frags<S, 0, kSwiglu>(f, g, 2);
   __builtin_amdgcn_sched_barrier(0);
-  mma<1>(c);
+  mma<1>(f);
   __builtin_amdgcn_sched_barrier(0);
-  read_frags<S, 1>(c, 3);
+  read_frags<S, 1, kSwiglu>(f, g, 3);
   __builtin_amdgcn_sched_barrier(0);
-  mma<0>(c);
+  mma<0>(f);
   __builtin_amdgcn_sched_barrier(0);
-  // k-tile kt+1 landed (only its prefetch may still be in flight); stage S
-  // fully read by this wave
-  __builtin_amdgcn_s_waitcnt(kWaitVm2Lgkm0);
+  if (wait_vm == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2, true));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(63, true));   // lgkm only
   lds_barrier();
-  read_frags<1 - S, 0>(c, 0);
-  issue_stage<S>(c, min(kt + 2, nk - 1));
-  prefetch_l2(c, min(kt + 2 + kPrefetchAhead, nk - 1));
+  if (wait_vm == 2) read_frags<1 - S, 0, kSwiglu>(f, g, 0);
+  if (issue) issue_stage<S>(g, dsrc, dkt);
+  if (pf) prefetch_l2(psrc, pkt);
   __builtin_amdgcn_sched_barrier(0);
-  mma<1>(c);
+  mma<1>(f);
   __builtin_amdgcn_sched_barrier(0);
 }
+
+// Tile L of the order: groups of kGroupM m-tiles x all n-tiles, m fastest.
+template <int kOutCols>
+__device__ __forceinline__ TileInfo tile_info(const GemmArgs& a, const int* pre, int total_m,
+                                              int NT, int L) {
+  const int group = L / (kGroupM * NT);
+  const int first = group * kGroupM;
+  const int gsz = min(total_m - first, kGroupM);
+  const int within = L - group * kGroupM * NT;
+  const int gm = first + within % gsz;
+  const int nt = within / gsz;
+  TileInfo t;
+  // block-uniform; say so, so that buffer resources live in scalar registers
+  t.e = __builtin_amdgcn_readfirstlane(find_expert(pre, a.E, gm));
+  const int mt = __builtin_amdgcn_readfirstlane(gm - pre[t.e]);
+  const int cnt = __builtin_amdgcn_readfirstlane(a.counts[t.e]);
+  t.row0 = __builtin_amdgcn_readfirstlane(a.offsets[t.e]) + mt * BM;
+  t.rows_valid = min(BM, cnt - mt * BM);
+  t.n0 = nt * kOutCols;
+  return t;
+}
+
+// DMA source of a tile for this wave. Every DMA address is in bounds by
+// construction: the A buffers (Xe, h) carry BM spare rows past R_cap, so a
+// tile may read BM rows from any segment start (rows past the segment only
+// feed discarded outputs), and a tile's weight rows never pass the expert's
+// 2I (or H) rows because I is a multiple of BN / 2 and H of BN. Row offsets
+// go in the scalar offset, so a lane keeps one offset register.
+template <bool kSwiglu>
+__device__ __forceinline__ TileSrc tile_src(const GemmArgs& a, const TileInfo& t, int I,
+                                            int wave, int ln) {
+  const int Kd = a.Kd;
+  const int64_t Nb = kSwiglu ? 2 * static_cast<int64_t>(I) : a.Nc;
+  TileSrc s;
+  const bool b_side = wave >> 1;
+  if (!b_side) {
+    const uint64_t left = (static_cast<uint64_t>(a.a_rows) - t.row0) * Kd * 2;
+    s.rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(t.row0) * Kd),
+        0, static_cast<int>(left < 0xffffffffull ? left : 0xffffffffull), kBufferFlags);
+  } else {
+    const uint64_t size = static_cast<uint64_t>(Nb) * Kd * 2;
+    s.rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(t.e) * Nb * Kd),
+        0, static_cast<int>(size < 0xffffffffull ? size : 0xffffffffull), kBufferFlags);
+  }
+  // this wave's 128 rows of its operand
+  int row0;
+  if (!b_side) row0 = (wave & 1) * (BM / 2);
+  else if (kSwiglu) row0 = (wave & 1) ? I + t.n0 : t.n0;          // gate | up
+  else row0 = t.n0 + (wave & 1) * (BN / 2);
+  // DMA j writes 1 KiB = 8 rows x 8 chunks: lane -> (row lane / 8, physical
+  // chunk lane % 8), fetching logical chunk (lane % 8) ^ (row % 8).
+  const int chunk = (ln & 7) ^ (ln >> 3);
+  s.voff = (static_cast<uint32_t>(row0 + (ln >> 3)) * Kd + chunk * 8) * 2;
+  s.stride = 8u * Kd * 2;
+  s.pf_off = static_cast<uint32_t>(row0 + ln) * Kd * 2;
+  s.pf_stride = static_cast<uint32_t>(kWave) * Kd * 2;
+  return s;
+}
+
 #endif  // __HIP_DEVICE_COMPILE__
 
 template <bool kSwiglu>
@@ -263,10 +330,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int Kd = a.Kd;
-  const int64_t Nb = kSwiglu ? 2 * static_cast<int64_t>(I) : a.Nc;
-  const uint16_t* __restrict__ Ab = static_cast<const uint16_t*>(a.A);
-  const uint16_t* __restrict__ Bb = static_cast<const uint16_t*>(a.B);
+  const int nk = a.Kd / BK;                 // even: H % 256 == 0, I % 128 == 0
   uint16_t* __restrict__ Cb = static_cast<uint16_t*>(a.C);
 
   // XCD-aware order: blocks are dealt round-robin to the 8 XCDs; give each
@@ -274,80 +338,51 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   const int G = gridDim.x;
   int pos = blockIdx.x;
   if ((G & 7) == 0) pos = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  if (pos >= total) return;
+
+  Geo g;
+  g.dma_dst = (wave >> 1) * kRegion + (wave & 1) * (BM / 2) * kCpr;
+#pragma unroll
+  for (int s = 0; s < BK / 16; ++s)
+    g.frag_ch[s] = (lane & 31) * kCpr + ((2 * s + (lane >> 5)) ^ (lane & 7));
+  g.a_frag = wm * 128 * kCpr;
+  g.b_frag = kRegion + (kSwiglu ? wn * 64 : wn * 128) * kCpr;
+
+  // Output geometry: acc[i][j][4 q' + q] is row (lane & 31) of row block i and
+  // column 8 q' + 4 (lane / 32) + q of weight block j; after pairing lanes l
+  // and l + 32 a lane holds 8 consecutive columns of one row.
+  constexpr int kStores = 4 * (kSwiglu ? 2 : 4) * 2;   // 16-byte stores per lane per tile
+
+  TileInfo t = tile_info<kOutCols>(a, pre, total_m, NT, pos);
+  TileSrc cur = tile_src<kSwiglu>(a, t, I, wave, lane);
+  issue_stage<0>(g, cur, 0);
+  prefetch_l2(cur, min(2, nk - 1));
+  issue_stage<1>(g, cur, 1);
+  prefetch_l2(cur, min(3, nk - 1));
+  bool first = true;
+  Frags f;
 
   for (int L = pos; L < total; L += G) {
-    // Lane geometry is recomputed per tile from an opaque copy of the lane id,
-    // so its registers are not held across the epilogue.
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-    TileCtx<kSwiglu> c;
-    // DMA geometry: waves 0-1 fill the A region, waves 2-3 the B region. DMA j
-    // of a wave writes 1 KiB = 8 rows x 8 chunks: lane -> (row lane / 8,
-    // physical chunk lane % 8), so the lane fetches logical chunk
-    // (lane % 8) ^ (row % 8) = (lane % 8) ^ (lane / 8).
-    const int dma_b = wave >> 1;
-    const int dma_row0 = (wave & 1) * (BM / 2) + (ln >> 3);     // + 8 j
-    const int dma_chunk = (ln & 7) ^ (ln >> 3);
-    c.dma_dst = dma_b * kRegion + (wave & 1) * (BM / 2) * kCpr;
-    // Fragments: lane reads row (lane & 31) of a 32-row block at logical
-    // chunk 2 s + lane / 32 in MFMA k-step s.
-#pragma unroll
-    for (int s = 0; s < kSub; ++s)
-      c.frag_ch[s] = (ln & 31) * kCpr + ((2 * s + (ln >> 5)) ^ (ln & 7));
-    c.a_frag = wm * 128 * kCpr;
-    c.b_frag = kRegion + (kSwiglu ? wn * 64 : wn * 128) * kCpr;
-
-    // tile order: groups of kGroupM m-tiles x all n-tiles, m fastest
-    const int group = L / (kGroupM * NT);
-    const int first = group * kGroupM;
-    const int gsz = min(total_m - first, kGroupM);
-    const int within = L - group * kGroupM * NT;
-    const int gm = first + within % gsz;
-    const int nt = within / gsz;
-    // tile parameters are block-uniform; say so, so that the buffer
-    // resources below live in scalar registers
-    const int e = __builtin_amdgcn_readfirstlane(find_expert(pre, a.E, gm));
-    const int mt = __builtin_amdgcn_readfirstlane(gm - pre[e]);
-    const int cnt = __builtin_amdgcn_readfirstlane(a.counts[e]);
-    const int row0 = __builtin_amdgcn_readfirstlane(a.offsets[e]) + mt * BM;
-    const int rows_valid = min(BM, cnt - mt * BM);
-    const int n0 = nt * kOutCols;
-
-    // Buffer resources over this tile's A rows and expert e's weights. Every
-    // DMA address is in bounds by construction: the A buffers (Xe, h) carry
-    // BM spare rows past R_cap, so a tile may read BM rows from any segment
-    // start (rows past the segment only feed discarded outputs), and the
-    // weight rows of a tile never pass the expert's 2I (or H) rows because I
-    // is a multiple of BN / 2 and H of BN. Row offsets go in the scalar
-    // offset, so a lane keeps a single offset register.
-    const uint64_t a_left = (static_cast<uint64_t>(a.a_rows) - row0) * Kd * 2;
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(Ab + static_cast<int64_t>(row0) * Kd), 0,
-        static_cast<int>(a_left < 0xffffffffull ? a_left : 0xffffffffull), kBufferFlags);
-    const uint64_t b_size = static_cast<uint64_t>(Nb) * Kd * 2;
-    const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(Bb + static_cast<int64_t>(e) * Nb * Kd), 0,
-        static_cast<int>(b_size < 0xffffffffull ? b_size : 0xffffffffull), kBufferFlags);
-    c.rsrc = dma_b ? rB : rA;
-    int row = dma_row0;                          // A: tile row of DMA 0
-    if (dma_b) {
-      if (kSwiglu) row = (wave & 1) ? I + n0 + (ln >> 3) : n0 + (ln >> 3);   // gate | up
-      else row = n0 + dma_row0;
+    const int Ln = L + G;
+    const bool has_next = Ln < total;
+    TileInfo tn = t;
+    TileSrc nxt = cur;
+    if (has_next) {
+      tn = tile_info<kOutCols>(a, pre, total_m, NT, Ln);
+      nxt = tile_src<kSwiglu>(a, tn, I, wave, lane);
     }
-    c.voff = (static_cast<uint32_t>(row) * Kd + dma_chunk * 8) * 2;
-    c.dma_stride = 8u * Kd * 2;
-    // prefetch rows: this wave's 128 rows of its operand, 64 per DMA
-    int pf_row = (wave & 1) * (BM / 2) + ln;                       // A tile row
-    if (dma_b) {
-      if (kSwiglu) pf_row = (wave & 1) ? I + n0 + ln : n0 + ln;   // gate | up
-      else pf_row = n0 + pf_row;
-    }
-    c.pf_off = static_cast<uint32_t>(pf_row) * Kd * 2;
-    c.pf_stride = static_cast<uint32_t>(kWave) * Kd * 2;
-    // Accumulators start at zero through an MFMA with zero operands: the
-    // result lands in accumulation registers directly, instead of 256 zeros
-    // built in ordinary vector registers first.
+
+    // k-tile 0 of this tile: DMA(0), pf(2), DMA(1), pf(3) and, after the
+    // first tile, the previous tile's output stores were issued after it.
+    if (first) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + 2 * kPfPerWave, false));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + 2 * kPfPerWave + kStores, false));
+    static_assert(kDmaPerWave + 2 * kPfPerWave + kStores <= 63, "vmcnt range");
+    first = false;
+    lds_barrier();
+    read_frags<0, 0, kSwiglu>(f, g, 0);
     {
+      // Accumulators start at zero through an MFMA with zero operands: the
+      // result lands in accumulation registers directly.
       bf16x8 zf;
       int zero = 0;
       asm volatile("" : "+v"(zero));
@@ -357,67 +392,66 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          c.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf, zf, floatx16{}, 0, 0, 0);
+          f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf, zf, floatx16{}, 0, 0, 0);
     }
 
     // Two LDS stages: k-tile kt+1 streams in while k-tile kt is multiplied.
-    // Tiles past the end re-read the last one (uniform control flow); their
-    // data is never used.
-    const int nk = Kd / BK;
-    issue_stage<0>(c, 0);
-    issue_stage<1>(c, min(1, nk - 1));
-    __builtin_amdgcn_s_waitcnt(kWaitVm16);      // k-tile 0 (own DMA)
-    prefetch_l2(c, min(2, nk - 1));
-    prefetch_l2(c, min(3, nk - 1));
-    lds_barrier();
-    read_frags<0, 0>(c, 0);
-    for (int kt = 0; kt < nk; kt += 2) {
-      ring_step<0>(c, kt, nk);
-      if (kt + 1 < nk) ring_step<1>(c, kt + 1, nk);
+    // The last two k-steps already request the next tile's first k-tiles.
+    for (int kt = 0; kt < nk - 2; kt += 2) {
+      const bool pf0 = kt + 4 < nk || has_next, pf1 = kt + 5 < nk || has_next;
+      const TileSrc& p0 = kt + 4 < nk ? cur : nxt;
+      const TileSrc& p1 = kt + 5 < nk ? cur : nxt;
+      const int pk0 = kt + 4 < nk ? kt + 4 : kt + 4 - nk;
+      const int pk1 = kt + 5 < nk ? kt + 5 : kt + 5 - nk;
+      ring_step<0, kSwiglu>(f, g, 2, true, cur, kt + 2, p0, pk0, pf0);
+      ring_step<1, kSwiglu>(f, g, 2, true, cur, kt + 3, p1, pk1, pf1);
     }
-    __builtin_amdgcn_s_waitcnt(0);              // drain the ring before reuse
-    __syncthreads();
+    ring_step<0, kSwiglu>(f, g, 2, has_next, nxt, 0, nxt, min(2, nk - 1), has_next);
+    ring_step<1, kSwiglu>(f, g, -1, has_next, nxt, 1, nxt, min(3, nk - 1), has_next);
 
-    // Epilogue: stage the bf16 tile in LDS row-major [BM][kOutCols] (rows
-    // split evenly over the two stage buffers), then write whole 16-byte
-    // chunks of rows. Lane owns column (lane & 31) of each 32x32 block and
-    // rows 8 (v / 4) + 4 (lane / 32) + (v % 4).
-    constexpr int kRowsPerStage = kStageUnits * 8 / kOutCols;   // 128 or 256
-    constexpr int kBlocksPerStage = kRowsPerStage / 32;          // 32-row blocks
-    // This wave's rows wm*128 + [0, 128) sit in buffer wm*128 / kRowsPerStage.
-    const int lane_off = 4 * (ln >> 5) * kOutCols + (kSwiglu ? wn * 64 : wn * 128) + (ln & 31);
-    uint16_t* ob = reinterpret_cast<uint16_t*>(stage_ptr_rt((wm * 128) / kRowsPerStage)) +
-                   ((wm * 128) % kRowsPerStage) * kOutCols + lane_off;
+    // Epilogue: bf16 (SwiGLU for the up projection) straight to global memory
+    // with buffer stores whose range check drops rows past the segment.
+    const uint64_t out_left = static_cast<uint64_t>(t.rows_valid) * a.Nc * 2;
+    const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
+        Cb + static_cast<int64_t>(t.row0) * a.Nc, 0, static_cast<int>(out_left), kBufferFlags);
+    const int hi = lane >> 5;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint16_t* base = ob + i * 32 * kOutCols;
+      const uint32_t row_off = static_cast<uint32_t>(wm * 128 + i * 32 + (lane & 31)) * a.Nc;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        uint16_t* orow = base + (8 * (v >> 2) + (v & 3)) * kOutCols;
-        if (kSwiglu) {
+      for (int j = 0; j < (kSwiglu ? 2 : 4); ++j) {
+        uint32_t d[4][2];   // [column group q'][pair]: bf16 pairs of 4 columns
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            orow[j * 32] = static_cast<uint16_t>(
-                f32_to_bf16_bits(silu_mul(c.acc[i][j][v], c.acc[i][j + 2][v])));
-        } else {
+        for (int qq = 0; qq < 4; ++qq) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            orow[j * 32] = static_cast<uint16_t>(f32_to_bf16_bits(c.acc[i][j][v]));
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int v0 = 4 * qq + 2 * h2, v1 = v0 + 1;
+            float x0, x1;
+            if (kSwiglu) {
+              x0 = silu_mul(f.acc[i][j][v0], f.acc[i][j + 2][v0]);
+              x1 = silu_mul(f.acc[i][j][v1], f.acc[i][j + 2][v1]);
+            } else {
+              x0 = f.acc[i][j][v0];
+              x1 = f.acc[i][j][v1];
+            }
+            d[qq][h2] = pack_bf16x2(x0, x1);
+          }
         }
-        // convert a few accumulators at a time: bounded register pressure
-        if ((v & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+        const int colj = t.n0 + (kSwiglu ? wn * 64 : wn * 128) + j * 32;
+#pragma unroll
+        for (int qq = 0; qq < 4; qq += 2) {
+          // lanes < 32 gather columns 8 qq + [0, 8), lanes >= 32 8 (qq+1) + [0, 8)
+          const auto s0 = __builtin_amdgcn_permlane32_swap(d[qq][0], d[qq + 1][0], false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(d[qq][1], d[qq + 1][1], false, false);
+          const u32x4 out = u32x4{s0[0], s1[0], s0[1], s1[1]};
+          const uint32_t col = colj + 8 * (qq + hi);
+          __builtin_amdgcn_raw_buffer_store_b128(out, rC, (row_off + col) * 2, 0, 0);
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    (void)kBlocksPerStage;
-    __syncthreads();
-    constexpr int kOutChunks = kOutCols / 8;   // 16-byte chunks per output row
-    for (int q = tid; q < BM * kOutChunks; q += kThreads) {
-      const int r = q / kOutChunks, ch = q % kOutChunks, col = n0 + ch * 8;
-      if (r < rows_valid && col < a.Nc)
-        *reinterpret_cast<u32x4*>(Cb + static_cast<int64_t>(row0 + r) * a.Nc + col) =
-            stage_ptr_rt(r / kRowsPerStage)[(r % kRowsPerStage) * kOutChunks + ch];
-    }
-    __syncthreads();
+    t = tn;
+    cur = nxt;
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }
