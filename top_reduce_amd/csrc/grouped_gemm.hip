@@ -107,7 +107,6 @@ constexpr int kRegion = BM * kCpr;                    // 16-byte units per opera
 constexpr int kStageUnits = 2 * kRegion;              // A then B: 64 KiB per stage
 constexpr int kWavesT = kThreads / kWave;             // 4
 constexpr int kDmaPerWave = kStageUnits / kWave / kWavesT;  // 16 x 1 KiB per wave per stage
-constexpr int kPfPerWave = 2;                         // L2-prefetch DMAs per wave per k-tile
 constexpr int kGroupM = 4;
 // Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
@@ -135,8 +134,6 @@ typedef __attribute__((address_space(3))) void lds_void;
 // into the other, so the compiler adds no wait for in-flight DMA before them.
 __shared__ u32x4 g_stage0[kStageUnits];
 __shared__ u32x4 g_stage1[kStageUnits];
-// Destination of the L2-prefetch DMAs: written, never read.
-__shared__ uint32_t g_prefetch_sink[kWave];
 
 template <int S>
 __device__ __forceinline__ u32x4* stage_ptr() { return S == 0 ? g_stage0 : g_stage1; }
@@ -151,8 +148,6 @@ struct TileSrc {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t voff;        // this lane's byte offset of DMA 0 of a k-tile
   uint32_t stride;      // bytes between the 8-row groups of DMA j and j + 1
-  uint32_t pf_off;      // this lane's row for the L2 prefetch, bytes
-  uint32_t pf_stride;   // bytes between the two 64-row prefetch groups
 };
 
 struct TileInfo {
@@ -179,14 +174,6 @@ __device__ __forceinline__ void issue_stage(const Geo& g, const TileSrc& src, in
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         src.rsrc, (lds_void*)(stage_ptr<S>() + g.dma_dst + j * 8 * kCpr), 16, src.voff,
         kt * BK * 2 + j * src.stride, 0, 0);
-}
-
-// Pull the lines of k-tile kt into L2: lane -> one row, one dword per line.
-__device__ __forceinline__ void prefetch_l2(const TileSrc& src, int kt) {
-#pragma unroll
-  for (int q = 0; q < kPfPerWave; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsrc, (lds_void*)g_prefetch_sink, 4, src.pf_off,
-                                             kt * BK * 2 + q * src.pf_stride, 0, 0);
 }
 
 // Fragments of MFMA k-step `sub` of stage S into register set P.
@@ -218,14 +205,13 @@ __device__ __forceinline__ void mma(Frags& f) {
 // register set 0, the next k-tile's DMA in flight into the other stage.
 // Fragment reads run one MFMA k-step ahead (the scheduling barriers keep the
 // compiler from sinking each read next to its use). Before the last k-step's
-// MFMAs the wave waits for the next k-tile (kWait: vmcnt allowance, or -1
-// when there is none), drains its LDS reads, meets the other waves, reads the
-// next k-tile's first fragments and refills stage S from `dsrc` (if any),
-// so the barrier hides behind 16 MFMAs.
+// MFMAs the wave waits for the next k-tile of this tile (if there is one),
+// drains its LDS reads, meets the other waves, reads that k-tile's first
+// fragments and refills stage S from `dsrc` (if `issue`), so the barrier
+// hides behind 16 MFMAs.
 template <int S, bool kSwiglu>
-__device__ __forceinline__ void ring_step(Frags& f, const Geo& g, int wait_vm, bool issue,
-                                          const TileSrc& dsrc, int dkt, const TileSrc& psrc,
-                                          int pkt, bool pf) {
+__device__ __forceinline__ void ring_step(Frags& f, const Geo& g, bool has_next_kt, bool issue,
+                                          const TileSrc& dsrc, int dkt) {
   read_frags<S, 1, kSwiglu>(f, g, 1);
   __builtin_amdgcn_sched_barrier(0);
   mma<0>(f);
@@ -238,21 +224,25 @@ __device__ __forceinline__ void ring_step(Frags& f, const Geo& g, int wait_vm, b
   __builtin_amdgcn_sched_barrier(0);
   mma<0>(f);
   __builtin_amdgcn_sched_barrier(0);
-  if (wait_vm == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2, true));
-  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(63, true));   // lgkm only
+  // the next k-tile's DMA is the only one in flight: vmcnt(0)
+  if (has_next_kt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, true));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(63, true));   // LDS reads only
   lds_barrier();
-  if (wait_vm == 2) read_frags<1 - S, 0, kSwiglu>(f, g, 0);
+  if (has_next_kt) read_frags<1 - S, 0, kSwiglu>(f, g, 0);
+  __builtin_amdgcn_sched_barrier(0);        // fragment reads before the refill
   if (issue) issue_stage<S>(g, dsrc, dkt);
-  if (pf) prefetch_l2(psrc, pkt);
   __builtin_amdgcn_sched_barrier(0);
   mma<1>(f);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Tile L of the order: groups of kGroupM m-tiles x all n-tiles, m fastest.
+// cnt_s / off_s: the experts' counts and segment offsets, copied to LDS so
+// that per-tile lookups are LDS reads, not vector loads (whose waits would
+// also wait for the DMA in flight).
 template <int kOutCols>
-__device__ __forceinline__ TileInfo tile_info(const GemmArgs& a, const int* pre, int total_m,
-                                              int NT, int L) {
+__device__ __forceinline__ TileInfo tile_info(const GemmArgs& a, const int* pre, const int* cnt_s,
+                                              const int* off_s, int total_m, int NT, int L) {
   const int group = L / (kGroupM * NT);
   const int first = group * kGroupM;
   const int gsz = min(total_m - first, kGroupM);
@@ -263,8 +253,8 @@ __device__ __forceinline__ TileInfo tile_info(const GemmArgs& a, const int* pre,
   // block-uniform; say so, so that buffer resources live in scalar registers
   t.e = __builtin_amdgcn_readfirstlane(find_expert(pre, a.E, gm));
   const int mt = __builtin_amdgcn_readfirstlane(gm - pre[t.e]);
-  const int cnt = __builtin_amdgcn_readfirstlane(a.counts[t.e]);
-  t.row0 = __builtin_amdgcn_readfirstlane(a.offsets[t.e]) + mt * BM;
+  const int cnt = __builtin_amdgcn_readfirstlane(cnt_s[t.e]);
+  t.row0 = __builtin_amdgcn_readfirstlane(off_s[t.e]) + mt * BM;
   t.rows_valid = min(BM, cnt - mt * BM);
   t.n0 = nt * kOutCols;
   return t;
@@ -304,8 +294,6 @@ __device__ __forceinline__ TileSrc tile_src(const GemmArgs& a, const TileInfo& t
   const int chunk = (ln & 7) ^ (ln >> 3);
   s.voff = (static_cast<uint32_t>(row0 + (ln >> 3)) * Kd + chunk * 8) * 2;
   s.stride = 8u * Kd * 2;
-  s.pf_off = static_cast<uint32_t>(row0 + ln) * Kd * 2;
-  s.pf_stride = static_cast<uint32_t>(kWave) * Kd * 2;
   return s;
 }
 
@@ -316,6 +304,11 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ int pre[kMaxE + 1];
   __shared__ int tmp[kWavesT];
+  __shared__ int cnt_s[kMaxE], off_s[kMaxE];
+  for (int e = threadIdx.x; e < a.E; e += kThreads) {
+    cnt_s[e] = a.counts[e];
+    off_s[e] = a.offsets[e];
+  }
 
   const int mode = a.mode;
   const int total_m = expert_prefix(a.counts, a.E, [mode](int c) {
@@ -353,12 +346,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   // and l + 32 a lane holds 8 consecutive columns of one row.
   constexpr int kStores = 4 * (kSwiglu ? 2 : 4) * 2;   // 16-byte stores per lane per tile
 
-  TileInfo t = tile_info<kOutCols>(a, pre, total_m, NT, pos);
+  TileInfo t = tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, pos);
   TileSrc cur = tile_src<kSwiglu>(a, t, I, wave, lane);
   issue_stage<0>(g, cur, 0);
-  prefetch_l2(cur, min(2, nk - 1));
   issue_stage<1>(g, cur, 1);
-  prefetch_l2(cur, min(3, nk - 1));
   bool first = true;
   Frags f;
 
@@ -368,15 +359,15 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     TileInfo tn = t;
     TileSrc nxt = cur;
     if (has_next) {
-      tn = tile_info<kOutCols>(a, pre, total_m, NT, Ln);
+      tn = tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, Ln);
       nxt = tile_src<kSwiglu>(a, tn, I, wave, lane);
     }
 
-    // k-tile 0 of this tile: DMA(0), pf(2), DMA(1), pf(3) and, after the
-    // first tile, the previous tile's output stores were issued after it.
-    if (first) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + 2 * kPfPerWave, false));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + 2 * kPfPerWave + kStores, false));
-    static_assert(kDmaPerWave + 2 * kPfPerWave + kStores <= 63, "vmcnt range");
+    // k-tile 0 of this tile: issued before DMA(1) and, after the first tile,
+    // before the previous tile's output stores.
+    if (first) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave, false));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + kStores, false));
+    static_assert(kDmaPerWave + kStores <= 63, "vmcnt range");
     first = false;
     lds_barrier();
     read_frags<0, 0, kSwiglu>(f, g, 0);
@@ -398,16 +389,11 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     // Two LDS stages: k-tile kt+1 streams in while k-tile kt is multiplied.
     // The last two k-steps already request the next tile's first k-tiles.
     for (int kt = 0; kt < nk - 2; kt += 2) {
-      const bool pf0 = kt + 4 < nk || has_next, pf1 = kt + 5 < nk || has_next;
-      const TileSrc& p0 = kt + 4 < nk ? cur : nxt;
-      const TileSrc& p1 = kt + 5 < nk ? cur : nxt;
-      const int pk0 = kt + 4 < nk ? kt + 4 : kt + 4 - nk;
-      const int pk1 = kt + 5 < nk ? kt + 5 : kt + 5 - nk;
-      ring_step<0, kSwiglu>(f, g, 2, true, cur, kt + 2, p0, pk0, pf0);
-      ring_step<1, kSwiglu>(f, g, 2, true, cur, kt + 3, p1, pk1, pf1);
+      ring_step<0, kSwiglu>(f, g, true, true, cur, kt + 2);
+      ring_step<1, kSwiglu>(f, g, true, true, cur, kt + 3);
     }
-    ring_step<0, kSwiglu>(f, g, 2, has_next, nxt, 0, nxt, min(2, nk - 1), has_next);
-    ring_step<1, kSwiglu>(f, g, -1, has_next, nxt, 1, nxt, min(3, nk - 1), has_next);
+    ring_step<0, kSwiglu>(f, g, true, has_next, nxt, 0);
+    ring_step<1, kSwiglu>(f, g, false, has_next, nxt, 1);
 
     // Epilogue: bf16 (SwiGLU for the up projection) straight to global memory
     // with buffer stores whose range check drops rows past the segment.
