@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
     ap.add_argument("--loop-only", action="store_true",
                     help="only warmup + timed steps (for profiler runs)")
+    ap.add_argument("--no-lowbatch", action="store_true",
+                    help="skip the low-batch combine-reduce measurement")
     return ap.parse_args()
 
 
@@ -80,6 +82,75 @@ def stored_traffic(kernel: str, config: str, src: str):
     if not (m_h and m_b) or m_h.group(1) != kernel_source_hash(src):
         return None
     return float(m_b.group(1))
+
+
+def lowbatch_combine(reps: int):
+    """Device time of moe_combine_reduce on the low-batch decode rows (H=3584,
+    top-16, 28 local experts, one real row in 8) at T = 1, 2, 4, 8 against
+    T = 64, for the stride routing (one local slot per real row) and the dense
+    stress variant (16 local slots per real row). Expert outputs are seeded
+    synthetic rows.
+
+    A Python call costs more than the kernel, so timing eager launches would
+    measure the host. The `reps` launches are captured once in a HIP graph
+    and the graph is replayed between two events on the replay stream: each
+    time is the mean over the launches of the replays, kernel execution plus
+    the graph's per-node dispatch gap. Every replay's output is compared
+    bit-for-bit with the eager launch."""
+    import numpy as np
+    import torch
+
+    import gen
+    import top_reduce_amd as tr
+
+    dev = torch.device("cuda:0")
+    reps = max(reps, 50)
+    replays = 5
+    out = {"unit": "us", "launches_per_graph": reps, "replays": replays,
+           "method": "HIP graph of back-to-back launches, events around the replays"}
+    for variant in ("", "dense"):
+        times = {}
+        for T in (1, 2, 4, 8, 64):
+            wl = gen.make_workload("c3", T=T, variant=variant)
+            idx = torch.from_numpy(wl.idx).to(dev)
+            w = torch.from_numpy(wl.weights).to(dev)
+            side = torch.cuda.Stream(dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                p = tr.plan(idx, E=wl.E, H=wl.H, I=wl.I, stream=side)
+                O = gen.make_expert_outputs(T * wl.K, wl.H, "bf16", seed=5)
+                Od = torch.from_numpy(O.view(np.int16)).view(torch.bfloat16).to(dev)
+                y_ref = torch.empty((T, wl.H), dtype=torch.bfloat16, device=dev)
+                tr.combine_reduce(p, w, y=y_ref, expert_out=Od, stream=side)
+                y = torch.zeros_like(y_ref)
+            side.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for _ in range(reps):
+                    tr.combine_reduce(p, w, y=y, expert_out=Od, stream=side)
+            torch.cuda.synchronize()
+            same = True
+            for _ in range(3):
+                y.zero_()
+                g.replay()
+                torch.cuda.synchronize()
+                same &= bool(torch.equal(y.view(torch.int16), y_ref.view(torch.int16)))
+            if not same:
+                raise RuntimeError(f"low-batch combine: graph replay differs from eager (T={T})")
+            st = torch.cuda.current_stream(dev)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(st)
+            for _ in range(replays):
+                g.replay()
+            b.record(st)
+            torch.cuda.synchronize()
+            times[T] = a.elapsed_time(b) / (reps * replays) * 1e3
+            del g
+        key = "stride" if variant == "" else "dense16"
+        out[key] = {str(T): round(t, 3) for T, t in times.items()}
+        out[key + "_ok"] = all(times[T] <= times[64] for T in (1, 2, 4, 8))
+    log(f"[bench] low-batch combine (us): {out}")
+    return out
 
 
 def main():
@@ -215,6 +286,9 @@ def main():
         "roofline": roofline,
         "stages": stages,
     }
+
+    if not args.no_lowbatch:
+        result["lowbatch_combine"] = lowbatch_combine(args.steps)
 
     # Sampled parity and the CPU oracle baseline on a bounded sample.
     if not (args.no_check and args.no_cpu_baseline):

@@ -171,6 +171,10 @@ def _route(spec: ConfigSpec, T: int, real: np.ndarray, rng) -> np.ndarray:
     if spec.routing == "stride_random":
         draw = lambda m: _distinct_uniform(rng, m, G, K)
         need_local = True
+    elif spec.routing == "stride_dense":
+        # stress variant: all K slots of a real row name distinct local experts
+        gidx[rows] = _distinct_uniform(rng, n, E, K)
+        return gidx
     elif spec.routing == "uniform":
         draw = lambda m: _distinct_uniform(rng, m, G, K)
         need_local = spec.need_local
@@ -199,17 +203,18 @@ def make_workload(name: str, T: Optional[int] = None, seed: Optional[int] = None
 
     ``T`` overrides the row count (c3 uses T in {1, 2, 4, 8, 64}; the others
     accept a smaller T for quick checks: rows are drawn the same way).
-    ``variant="random"`` selects the random routing variant of c3; for c3 the
-    default seed is 103 + T (+1000 for the random variant).
+    ``variant="random"`` selects the random routing variant of c3 and
+    ``variant="dense"`` its stress variant (all 16 slots of a real row local);
+    for c3 the default seed is 103 + T (+1000 random, +2000 dense).
     """
     spec = CONFIGS[name]
-    if variant == "random":
+    if variant in ("random", "dense"):
         if name != "c3":
-            raise ValueError("the random variant exists for c3 only")
-        spec = dataclasses.replace(spec, routing="stride_random")
+            raise ValueError(f"the {variant} variant exists for c3 only")
+        spec = dataclasses.replace(spec, routing="stride_" + variant)
     T = spec.T if T is None else int(T)
     if seed is None:
-        seed = spec.seed + (T if name == "c3" else 0) + (1000 if variant == "random" else 0)
+        seed = spec.seed + (T if name == "c3" else 0) + {"": 0, "random": 1000, "dense": 2000}[variant]
     s_route, s_logit, s_x, _, _ = _streams(seed, spec.E)
 
     if name == "c3":
@@ -225,7 +230,7 @@ def make_workload(name: str, T: Optional[int] = None, seed: Optional[int] = None
     gidx = _route(spec, T, real, np.random.default_rng(s_route))
 
     K = spec.K
-    if spec.routing in ("stride", "stride_random"):
+    if spec.routing in ("stride", "stride_random", "stride_dense"):
         weights = np.zeros((T, K), dtype=np.float32)
         weights[real] = np.float32(1.0 / K)
     else:

@@ -53,7 +53,7 @@ def test_forward_full_compare(name, flags):
 
 
 @pytest.mark.parametrize("T", [1, 2, 4, 8, 64])
-@pytest.mark.parametrize("variant", ["", "random"])
+@pytest.mark.parametrize("variant", ["", "random", "dense"])
 def test_forward_c3_decode(T, variant):
     say(f"forward c3 T={T} {variant}")
     wl = gen.make_workload("c3", T=T, variant=variant, with_weights=True)
