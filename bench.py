@@ -1,15 +1,16 @@
 #!/usr/bin/env python3
 """Throughput of one GPU's share of the expert-parallel MoE FFN on MI355X.
 
-One step = the whole hot path on one batch: moe_plan (route scan) +
-moe_forward (expand, grouped SwiGLU GEMM up/down, weighted top-k reduce), on
-synthetic inputs already resident in HBM. Default workload: the prefill shape
+One step = the whole hot path on one batch: moe_plan (route scan), then the
+four kernels moe_forward runs (expand, grouped SwiGLU GEMM up and down,
+weighted top-k reduce) through their stage entry points, on synthetic inputs
+already resident in HBM. Default workload: the prefill shape
 (16384 received tokens, H=7168, I=2048, 32 local experts of 256, top-8, Zipf
 s=1.0 popularity), bf16.
 
 Prints ONE JSON line: tokens/s over the timed steps, the roofline of the
-dominant kernel (HIP events on the stream the kernels run on), per-stage
-rates, a sampled parity check and the CPU oracle's rate on a bounded sample
+dominant kernel (HIP events between the stages of every timed step, on the
+stream the kernels run on), per-stage rates, the low-batch combine latencies, a sampled parity check and the CPU oracle's rate on a bounded sample
 of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config c5] [--gpus 1]
@@ -61,6 +62,8 @@ def parse():
                     help="only warmup + timed steps (for profiler runs)")
     ap.add_argument("--no-lowbatch", action="store_true",
                     help="skip the low-batch combine-reduce measurement")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run a plain elementwise copy of this many MiB first (counter calibration)")
     return ap.parse_args()
 
 
@@ -200,14 +203,49 @@ def main():
     real_rows = int(wl.real.sum())
     log(f"[bench] R={R} T_loc={T_loc} real_rows={real_rows} empty_experts={n_empty}")
 
+    if args.copy_calibration_mib:
+        # A plain elementwise kernel over a known number of bytes: its HBM
+        # counters calibrate the counters of the path's kernels.
+        n = args.copy_calibration_mib * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] copy calibration: torch.neg over {n * 2} bytes read + {n * 2} written, x3")
+        del src, dst
+
+    # One step = plan (route scan) + forward (expand, grouped GEMM up and
+    # down, combine-reduce): the same kernels moe_forward launches, called
+    # stage by stage so that events between the stages, on the launch stream,
+    # give each kernel's device time inside the timed region.
+    stage_names = ("route_scan", "expand", "gemm_up", "gemm_down", "combine_reduce")
+
+    def staged_step(evs):
+        evs[0].record(stream)
+        q = tr.plan(idx, E=wl.E, H=wl.H, I=wl.I, dtype=tdt, ws=ws, stream=stream)
+        evs[1].record(stream)
+        tr.expand(q, x, stream=stream)
+        evs[2].record(stream)
+        tr.grouped_gemm_up(q, w1, stream=stream)
+        evs[3].record(stream)
+        tr.grouped_gemm_down(q, w2, stream=stream)
+        evs[4].record(stream)
+        tr.combine_reduce(q, w, y=y, stream=stream)
+        evs[5].record(stream)
+
+    def new_events():
+        return [torch.cuda.Event(enable_timing=True) for _ in range(len(stage_names) + 1)]
+
     for _ in range(args.warmup):
-        step()
+        staged_step(new_events())
     torch.cuda.synchronize()
+    step_events = [new_events() for _ in range(args.steps)]
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(args.steps):
-        step()
+    for evs in step_events:
+        staged_step(evs)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -220,34 +258,15 @@ def main():
         print(json.dumps({"metric": METRIC, "value": tokens_per_s, "unit": "tokens/s",
                           "ms_per_step": ms_step, "loop_only": True}), flush=True)
         return
-
-    # Per-stage device time: each stage alone, args.steps launches between two
-    # events on the same stream.
-    def timed(fn, n=None):
-        n = n or args.steps
-        fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(n):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / n * 1e3          # us per launch
-
-    us = {
-        "route_scan": timed(lambda: tr.plan(idx, E=wl.E, H=wl.H, I=wl.I, dtype=tdt, ws=ws, stream=stream)),
-        "expand": timed(lambda: tr.expand(p, x, stream=stream)),
-        "gemm_up": timed(lambda: tr.grouped_gemm_up(p, w1, stream=stream)),
-        "gemm_down": timed(lambda: tr.grouped_gemm_down(p, w2, stream=stream)),
-        "combine_reduce": timed(lambda: tr.combine_reduce(p, w, y=y, stream=stream)),
-    }
+    # mean device time of each stage over the timed steps, us per launch
+    us = {name: sum(evs[i].elapsed_time(evs[i + 1]) for evs in step_events) / args.steps * 1e3
+          for i, name in enumerate(stage_names)}
     b = 2 if bf16 else 4
     H, I, T, K = wl.H, wl.I, wl.T, wl.K
     peak_mm = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     work = {
         # algorithmic bytes / flops per launch
-        "expand": ("hbm", (T_loc + R) * H * b + 4 * R),
+        "expand": ("hbm", (T_loc + R) * H * b + 4 * T * K),
         "gemm_up": ("mfma" if bf16 else "alu", 4.0 * R * H * I),
         "gemm_down": ("mfma" if bf16 else "alu", 2.0 * R * H * I),
         "combine_reduce": ("hbm", R * H * b + T * H * b + 8 * T * K),

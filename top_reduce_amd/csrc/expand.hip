@@ -1,13 +1,13 @@
 // moe_expand: copy each received row once per local route into the
-// expert-contiguous buffer, Xe[r] = x[row_src[r]] (DeepEP issue #48 answer:
+// expert-contiguous buffer, Xe[row_map[t, k]] = x[t] (DeepEP issue #48 answer:
 // with a grouped GEMM one token must be expanded to several experts).
 //
-// HBM-bound row gather. The number of rows R lives on the device
-// (offsets[E]); the grid is sized for the upper bound and every wave walks
-// 1 KiB slabs (64 lanes x 16 bytes) of rows with a grid stride, so there is
-// no host sync and no per-row launch cost. The source row index is
-// wave-uniform (scalar load); each wave keeps kUnroll 16-byte loads in
-// flight before storing.
+// HBM-bound scatter in received order. A wave owns one token at a time: it
+// reads the token's slot map (scalar loads), skips the token if no slot is
+// local (padding rows cost one map read), loads up to kBatch 1 KiB slabs of
+// the row (64 lanes x 16 bytes) and stores them to every local slot's row.
+// Each input row is read from HBM once however many local experts it has;
+// rows are walked with a grid stride, so there is no host sync.
 #include "tr_device.h"
 #include "tr_internal.h"
 
@@ -15,38 +15,40 @@ namespace tr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kBatch = 8;
 
 __global__ __launch_bounds__(kThreads) void expand_rows(const u32x4* __restrict__ x,
-                                                        const int* __restrict__ row_src,
-                                                        const int* __restrict__ R_ptr,
-                                                        int64_t chunks, u32x4* __restrict__ Xe) {
-  const int64_t R = *R_ptr;
-  const int64_t nslab = (chunks + kWave - 1) / kWave;
-  const int64_t items = R * nslab;
+                                                        const int* __restrict__ row_map, int64_t T,
+                                                        int K, int64_t chunks,
+                                                        u32x4* __restrict__ Xe) {
   const int lane = lane_id();
-  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
+  const int64_t gw = __builtin_amdgcn_readfirstlane(
+      static_cast<int>((static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave));
   const int64_t nw = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  for (int64_t it = gw * kUnroll; it < items; it += nw * kUnroll) {
-    u32x4 v[kUnroll];
-    int64_t dst[kUnroll];
+  for (int64_t t = gw; t < T; t += nw) {
+    const int* rm = row_map + t * K;
+    bool any = false;
+    for (int k = 0; k < K; ++k) any |= rm[k] >= 0;
+    if (!any) continue;
+    const u32x4* src = x + t * chunks;
+    for (int64_t c0 = 0; c0 < chunks; c0 += kBatch * kWave) {
+      u32x4 v[kBatch];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      dst[u] = -1;
-      const int64_t item = it + u;
-      if (item < items) {
-        const int r = __builtin_amdgcn_readfirstlane(static_cast<int>(item / nslab));
-        const int64_t c = (item - static_cast<int64_t>(r) * nslab) * kWave + lane;
-        const int src = row_src[r];
-        if (c < chunks) {
-          v[u] = x[static_cast<int64_t>(src) * chunks + c];
-          dst[u] = static_cast<int64_t>(r) * chunks + c;
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t c = c0 + u * kWave + lane;
+        if (c < chunks) v[u] = src[c];
+      }
+      for (int k = 0; k < K; ++k) {
+        const int r = rm[k];
+        if (r < 0) continue;
+        u32x4* dst = Xe + static_cast<int64_t>(r) * chunks;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int64_t c = c0 + u * kWave + lane;
+          if (c < chunks) dst[c] = v[u];
         }
       }
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (dst[u] >= 0) Xe[dst[u]] = v[u];
   }
 }
 
@@ -55,14 +57,12 @@ __global__ __launch_bounds__(kThreads) void expand_rows(const u32x4* __restrict_
 hipError_t expand(const tr_moe_plan& p, const void* x, hipStream_t st) {
   const int64_t es = p.d.dtype == TR_BF16 ? 2 : 4;
   const int64_t chunks = p.d.H * es / 16;
-  const int64_t nslab = (chunks + kWave - 1) / kWave;
-  const int64_t waves = cdiv(p.R_cap * nslab, kUnroll);
-  int64_t blocks = cdiv(waves, kThreads / kWave);
-  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 16;
+  int64_t blocks = cdiv(p.d.T, kThreads / kWave);
+  const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(expand_rows, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, st,
-                     static_cast<const u32x4*>(x), p.row_src, p.offsets + p.d.E, chunks,
+                     static_cast<const u32x4*>(x), p.row_map, p.d.T, p.d.K, chunks,
                      static_cast<u32x4*>(p.Xe));
   return hipGetLastError();
 }

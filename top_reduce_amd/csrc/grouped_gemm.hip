@@ -108,6 +108,9 @@ constexpr int kStageUnits = 2 * kRegion;              // A then B: 64 KiB per st
 constexpr int kWavesT = kThreads / kWave;             // 4
 constexpr int kDmaPerWave = kStageUnits / kWave / kWavesT;  // 16 x 1 KiB per wave per stage
 constexpr int kGroupM = 4;
+#ifndef TR_GEMM_SPLIT_FIRST
+#define TR_GEMM_SPLIT_FIRST 8
+#endif
 // Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
@@ -166,14 +169,19 @@ struct Frags {
   floatx16 acc[4][4];          // acc[i][j]: weight block j x row block i
 };
 
-// Stage S <- k-tile kt of `src`: 16 DMA of 1 KiB (8 rows x 128 B) per wave.
+// DMA j (1 KiB = 8 rows x 128 B) of stage S <- k-tile kt of `src`.
+template <int S>
+__device__ __forceinline__ void issue_one(const Geo& g, const TileSrc& src, int kt, int j) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      src.rsrc, (lds_void*)(stage_ptr<S>() + g.dma_dst + j * 8 * kCpr), 16, src.voff,
+      kt * BK * 2 + j * src.stride, 0, 0);
+}
+
+// Stage S <- k-tile kt of `src`: all 16 DMA of this wave.
 template <int S>
 __device__ __forceinline__ void issue_stage(const Geo& g, const TileSrc& src, int kt) {
 #pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        src.rsrc, (lds_void*)(stage_ptr<S>() + g.dma_dst + j * 8 * kCpr), 16, src.voff,
-        kt * BK * 2 + j * src.stride, 0, 0);
+  for (int j = 0; j < kDmaPerWave; ++j) issue_one<S>(g, src, kt, j);
 }
 
 // Fragments of MFMA k-step `sub` of stage S into register set P.
@@ -201,20 +209,51 @@ __device__ __forceinline__ void mma(Frags& f) {
       f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fb[P][j], f.fa[P][i], f.acc[i][j], 0, 0, 0);
 }
 
+// The 16 MFMAs of register set P with kN DMAs (j0 .. j0 + kN - 1 of stage
+// S <- k-tile kt of `src`, if `issue`) spread evenly between them: a burst of
+// DMA issues would hold up the wave's MFMA issue while the address path
+// drains.
+template <int P, int S, int kN>
+__device__ __forceinline__ void mma_dma(Frags& f, bool issue, const Geo& g, const TileSrc& src,
+                                        int kt, int j0) {
+  static_assert(kN == 0 || 16 % kN == 0, "DMAs must spread evenly over 16 MFMAs");
+  constexpr int kEvery = kN ? 16 / kN : 16;
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int i = m >> 2, j = m & 3;
+    f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fb[P][j], f.fa[P][i], f.acc[i][j], 0, 0, 0);
+    if (kN && m % kEvery == kEvery - 1) {
+      if (issue) issue_one<S>(g, src, kt, j0 + m / kEvery);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Refill DMAs of a stage are split: kSplitFirst of them go between the last
+// k-step's MFMAs of the step that frees the stage, the rest between the first
+// k-step's MFMAs of the following step.
+constexpr int kSplitFirst = TR_GEMM_SPLIT_FIRST;
+static_assert(kSplitFirst == 8 || kSplitFirst == 16, "refill split: 8 + 8 or 16 + 0");
+
 // One k-tile held in stage S, its first k-step's fragments already in
 // register set 0, the next k-tile's DMA in flight into the other stage.
 // Fragment reads run one MFMA k-step ahead (the scheduling barriers keep the
-// compiler from sinking each read next to its use). Before the last k-step's
-// MFMAs the wave waits for the next k-tile of this tile (if there is one),
-// drains its LDS reads, meets the other waves, reads that k-tile's first
-// fragments and refills stage S from `dsrc` (if `issue`), so the barrier
-// hides behind 16 MFMAs.
-template <int S, bool kSwiglu>
-__device__ __forceinline__ void ring_step(Frags& f, const Geo& g, bool has_next_kt, bool issue,
+// compiler from sinking each read next to its use). The first k-step's MFMAs
+// carry the rest of the other stage's refill (`pend`: DMAs kSplitFirst..15 of
+// k-tile pkt of `psrc`). Before the last k-step's MFMAs the wave waits for
+// the next k-tile of this tile (if there is one), drains its LDS reads, meets
+// the other waves and reads that k-tile's first fragments; the last k-step's
+// MFMAs then carry the first DMAs of stage S's refill from `dsrc` (all 16 if
+// kLast).
+template <int S, bool kSwiglu, bool kLast>
+__device__ __forceinline__ void ring_step(Frags& f, const Geo& g, bool has_next_kt, bool pend,
+                                          const TileSrc& psrc, int pkt, bool issue,
                                           const TileSrc& dsrc, int dkt) {
+  constexpr int kFirst = kLast ? kDmaPerWave : kSplitFirst;
+  constexpr int kRest = kDmaPerWave - kSplitFirst;
   read_frags<S, 1, kSwiglu>(f, g, 1);
   __builtin_amdgcn_sched_barrier(0);
-  mma<0>(f);
+  mma_dma<0, 1 - S, kRest>(f, pend, g, psrc, pkt, kSplitFirst);
   __builtin_amdgcn_sched_barrier(0);
   read_frags<S, 0, kSwiglu>(f, g, 2);
   __builtin_amdgcn_sched_barrier(0);
@@ -230,9 +269,7 @@ __device__ __forceinline__ void ring_step(Frags& f, const Geo& g, bool has_next_
   lds_barrier();
   if (has_next_kt) read_frags<1 - S, 0, kSwiglu>(f, g, 0);
   __builtin_amdgcn_sched_barrier(0);        // fragment reads before the refill
-  if (issue) issue_stage<S>(g, dsrc, dkt);
-  __builtin_amdgcn_sched_barrier(0);
-  mma<1>(f);
+  mma_dma<1, S, kFirst>(f, issue, g, dsrc, dkt, 0);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -388,12 +425,18 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
 
     // Two LDS stages: k-tile kt+1 streams in while k-tile kt is multiplied.
     // The last two k-steps already request the next tile's first k-tiles.
-    for (int kt = 0; kt < nk - 2; kt += 2) {
-      ring_step<0, kSwiglu>(f, g, true, true, cur, kt + 2);
-      ring_step<1, kSwiglu>(f, g, true, true, cur, kt + 3);
+    // Step kt refills its stage with k-tile kt + 2 (of the next tile past the
+    // end) and finishes the refill that step kt - 1 began.
+    constexpr bool kSplit = kSplitFirst < kDmaPerWave;
+    ring_step<0, kSwiglu, false>(f, g, true, false, cur, 0, nk > 2 || has_next,
+                                 nk > 2 ? cur : nxt, nk > 2 ? 2 : 0);
+    if (nk > 2) ring_step<1, kSwiglu, false>(f, g, true, kSplit, cur, 2, true, cur, 3);
+    for (int kt = 2; kt < nk - 2; kt += 2) {
+      ring_step<0, kSwiglu, false>(f, g, true, kSplit, cur, kt + 1, true, cur, kt + 2);
+      ring_step<1, kSwiglu, false>(f, g, true, kSplit, cur, kt + 2, true, cur, kt + 3);
     }
-    ring_step<0, kSwiglu>(f, g, true, has_next, nxt, 0);
-    ring_step<1, kSwiglu>(f, g, false, has_next, nxt, 1);
+    if (nk > 2) ring_step<0, kSwiglu, false>(f, g, true, kSplit, cur, nk - 1, has_next, nxt, 0);
+    ring_step<1, kSwiglu, true>(f, g, false, kSplit && has_next, nxt, 0, has_next, nxt, 1);
 
     // Epilogue: bf16 (SwiGLU for the up projection) straight to global memory
     // with buffer stores whose range check drops rows past the segment.
