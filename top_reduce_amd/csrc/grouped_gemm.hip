@@ -15,8 +15,9 @@
 //
 //  - gemm_tiled: persistent 256x256x64 block tiles on bf16 MFMA
 //    (v_mfma_f32_32x32x16_bf16), four waves each owning a 128x128 quadrant,
-//    operands staged through XOR-swizzled LDS with a register prefetch of the
-//    next k-tile. Tiles are numbered expert-major with groups of 4 m-tiles and
+//    operands staged through two XOR-swizzled LDS stages: activation rows by
+//    buffer->LDS DMA one k-tile ahead, weight rows through registers loaded
+//    four k-tiles ahead. Tiles are numbered expert-major with groups of 4 m-tiles and
 //    handed to the 8 XCDs in contiguous chunks so that concurrent tiles of an
 //    XCD share A and B tiles in its L2. For GEMM1 each B tile holds 128 gate
 //    rows and the matching 128 up rows, so a lane owns gate and up of the
@@ -104,13 +105,8 @@ static_assert(BM <= kRowPad, "A buffers must carry BM spare rows");
 static_assert(BN == kColMultiple, "the H granularity must match the tile");
 constexpr int kCpr = BK / 8;                          // 16-byte chunks per tile row (8)
 constexpr int kRegion = BM * kCpr;                    // 16-byte units per operand per stage
-constexpr int kStageUnits = 2 * kRegion;              // A then B: 64 KiB per stage
 constexpr int kWavesT = kThreads / kWave;             // 4
-constexpr int kDmaPerWave = kStageUnits / kWave / kWavesT;  // 16 x 1 KiB per wave per stage
 constexpr int kGroupM = 4;
-#ifndef TR_GEMM_SPLIT_FIRST
-#define TR_GEMM_SPLIT_FIRST 8
-#endif
 // Word 3 of a raw buffer resource on gfx950 (32-bit data format, no swizzle).
 constexpr int kBufferFlags = 0x00020000;
 
@@ -133,24 +129,37 @@ __host__ __device__ constexpr int waitcnt_vm(int n, bool lgkm0) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Two LDS stages as distinct objects: reads of one provably do not alias DMA
-// into the other, so the compiler adds no wait for in-flight DMA before them.
-__shared__ u32x4 g_stage0[kStageUnits];
-__shared__ u32x4 g_stage1[kStageUnits];
+// Two LDS stages, each an activation half and a weight half, all distinct
+// objects: an access to one provably does not alias DMA into another, so the
+// compiler adds no wait for in-flight DMA before it.
+__shared__ u32x4 g_a0[kRegion], g_b0[kRegion];
+__shared__ u32x4 g_a1[kRegion], g_b1[kRegion];
 
 template <int S>
-__device__ __forceinline__ u32x4* stage_ptr() { return S == 0 ? g_stage0 : g_stage1; }
+__device__ __forceinline__ u32x4* stage_a() { return S == 0 ? g_a0 : g_a1; }
+template <int S>
+__device__ __forceinline__ u32x4* stage_b() { return S == 0 ? g_b0 : g_b1; }
 
 // The buffer-resource type exists only in the device compilation pass, so
 // the tile state and the pipeline helpers are device-pass only.
 #if defined(__HIP_DEVICE_COMPILE__)
 
-// Where one tile's operands come from: this wave's DMA source (A rows for
-// waves 0-1, weight rows for waves 2-3).
+// Operand staging. Each wave moves 8 pieces (1 KiB = 8 rows x 128 B each) of
+// the activation tile and 8 of the weight tile per k-tile. The activation
+// pieces go straight to LDS by buffer->LDS DMA, issued once the stage is free
+// (one k-step to land). The weight pieces go through registers: loaded four
+// k-tiles ahead, written to LDS two k-steps later (two k-steps to land).
+// Weight rows are the larger share of the L2 misses. The limit here is the
+// number of requests a CU keeps in flight times their L2 latency, so deeper
+// staging (both operands through registers) measured no faster.
+constexpr int kPieces = 8;
+constexpr bool kRegActs = false;   // weights through registers, activations by DMA
+
+// Where one tile's operands come from, for this wave and lane.
 struct TileSrc {
-  __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t voff;        // this lane's byte offset of DMA 0 of a k-tile
-  uint32_t stride;      // bytes between the 8-row groups of DMA j and j + 1
+  __amdgpu_buffer_rsrc_t d_rsrc, r_rsrc;   // DMA operand, register operand
+  uint32_t d_voff, r_voff;  // this lane's byte offset of piece 0 of k-tile 0
+  uint32_t stride;          // bytes between pieces j and j + 1 (8 rows)
 };
 
 struct TileInfo {
@@ -159,7 +168,8 @@ struct TileInfo {
 
 // Lane geometry, fixed for the whole kernel.
 struct Geo {
-  int dma_dst;          // 16-byte unit of DMA 0 in a stage
+  int d_dst;            // 16-byte unit of this wave's DMA piece 0 (DMA base)
+  int r_dst;            // 16-byte unit of this lane's part of register piece 0
   int a_frag, b_frag;   // 16-byte unit of this wave's first A / B fragment row
   int frag_ch[BK / 16]; // per MFMA k-step: row-in-block * 8 + swizzled chunk
 };
@@ -169,32 +179,23 @@ struct Frags {
   floatx16 acc[4][4];          // acc[i][j]: weight block j x row block i
 };
 
-// DMA j (1 KiB = 8 rows x 128 B) of stage S <- k-tile kt of `src`.
-template <int S>
-__device__ __forceinline__ void issue_one(const Geo& g, const TileSrc& src, int kt, int j) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      src.rsrc, (lds_void*)(stage_ptr<S>() + g.dma_dst + j * 8 * kCpr), 16, src.voff,
-      kt * BK * 2 + j * src.stride, 0, 0);
-}
-
-// Stage S <- k-tile kt of `src`: all 16 DMA of this wave.
-template <int S>
-__device__ __forceinline__ void issue_stage(const Geo& g, const TileSrc& src, int kt) {
-#pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j) issue_one<S>(g, src, kt, j);
-}
+// One wave's weight pieces of a k-tile, in registers.
+struct Regs {
+  u32x4 v[kPieces];
+};
 
 // Fragments of MFMA k-step `sub` of stage S into register set P.
 template <int S, int P, bool kSwiglu>
 __device__ __forceinline__ void read_frags(Frags& f, const Geo& g, int sub) {
-  const u32x4* base = stage_ptr<S>();
+  const u32x4* sa = stage_a<S>();
+  const u32x4* sb = stage_b<S>();
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    f.fa[P][i] = __builtin_bit_cast(bf16x8, base[g.a_frag + i * 32 * kCpr + g.frag_ch[sub]]);
+    f.fa[P][i] = __builtin_bit_cast(bf16x8, sa[g.a_frag + i * 32 * kCpr + g.frag_ch[sub]]);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int rb = kSwiglu ? (j < 2 ? j * 32 : 128 + (j - 2) * 32) : j * 32;
-    f.fb[P][j] = __builtin_bit_cast(bf16x8, base[g.b_frag + rb * kCpr + g.frag_ch[sub]]);
+    f.fb[P][j] = __builtin_bit_cast(bf16x8, sb[g.b_frag + rb * kCpr + g.frag_ch[sub]]);
   }
 }
 
@@ -209,51 +210,64 @@ __device__ __forceinline__ void mma(Frags& f) {
       f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fb[P][j], f.fa[P][i], f.acc[i][j], 0, 0, 0);
 }
 
-// The 16 MFMAs of register set P with kN DMAs (j0 .. j0 + kN - 1 of stage
-// S <- k-tile kt of `src`, if `issue`) spread evenly between them: a burst of
-// DMA issues would hold up the wave's MFMA issue while the address path
-// drains.
-template <int P, int S, int kN>
-__device__ __forceinline__ void mma_dma(Frags& f, bool issue, const Geo& g, const TileSrc& src,
-                                        int kt, int j0) {
-  static_assert(kN == 0 || 16 % kN == 0, "DMAs must spread evenly over 16 MFMAs");
-  constexpr int kEvery = kN ? 16 / kN : 16;
+template <int S>
+__device__ __forceinline__ u32x4* dma_stage() { return kRegActs ? stage_b<S>() : stage_a<S>(); }
+template <int S>
+__device__ __forceinline__ u32x4* reg_stage() { return kRegActs ? stage_a<S>() : stage_b<S>(); }
+
+template <int S>
+__device__ __forceinline__ void dma_a(const Geo& g, const TileSrc& s, int kt, int j) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      s.d_rsrc, (lds_void*)(dma_stage<S>() + g.d_dst + j * 8 * kCpr), 16, s.d_voff,
+      kt * BK * 2 + j * s.stride, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 load_b(const TileSrc& s, int kt, int j) {
+  return __builtin_amdgcn_raw_buffer_load_b128(s.r_rsrc, s.r_voff, kt * BK * 2 + j * s.stride, 0);
+}
+
+template <int S>
+__device__ __forceinline__ void write_b(const Geo& g, const u32x4& v, int j) {
+  reg_stage<S>()[g.r_dst + j * 8 * kCpr] = v;
+}
+
+// The 16 MFMAs of register set P with the refill of stage S between them:
+// first the 8 activation DMAs of k-tile `dkt` of `ds`, then the 8 weight
+// pieces of k-tile kt + 2 from `r` into the stage, each followed by the
+// reload of its register with k-tile `lkt` of `ls`. Spreading the issues
+// keeps the MFMA pipe fed; the compiler's per-register waits gate each LDS
+// write on its own load only.
+template <int P, int S>
+__device__ __forceinline__ void mma_io(Frags& f, Regs& r, const Geo& g, const TileSrc& ds, int dkt,
+                                       const TileSrc& ls, int lkt) {
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
     const int i = m >> 2, j = m & 3;
     f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fb[P][j], f.fa[P][i], f.acc[i][j], 0, 0, 0);
-    if (kN && m % kEvery == kEvery - 1) {
-      if (issue) issue_one<S>(g, src, kt, j0 + m / kEvery);
-      __builtin_amdgcn_sched_barrier(0);
+    if (m < kPieces) {
+      dma_a<S>(g, ds, dkt, m);
+    } else {
+      write_b<S>(g, r.v[m - kPieces], m - kPieces);
+      r.v[m - kPieces] = load_b(ls, lkt, m - kPieces);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Refill DMAs of a stage are split: kSplitFirst of them go between the last
-// k-step's MFMAs of the step that frees the stage, the rest between the first
-// k-step's MFMAs of the following step.
-constexpr int kSplitFirst = TR_GEMM_SPLIT_FIRST;
-static_assert(kSplitFirst == 8 || kSplitFirst == 16, "refill split: 8 + 8 or 16 + 0");
-
 // One k-tile held in stage S, its first k-step's fragments already in
-// register set 0, the next k-tile's DMA in flight into the other stage.
-// Fragment reads run one MFMA k-step ahead (the scheduling barriers keep the
-// compiler from sinking each read next to its use). The first k-step's MFMAs
-// carry the rest of the other stage's refill (`pend`: DMAs kSplitFirst..15 of
-// k-tile pkt of `psrc`). Before the last k-step's MFMAs the wave waits for
-// the next k-tile of this tile (if there is one), drains its LDS reads, meets
-// the other waves and reads that k-tile's first fragments; the last k-step's
-// MFMAs then carry the first DMAs of stage S's refill from `dsrc` (all 16 if
-// kLast).
-template <int S, bool kSwiglu, bool kLast>
-__device__ __forceinline__ void ring_step(Frags& f, const Geo& g, bool has_next_kt, bool pend,
-                                          const TileSrc& psrc, int pkt, bool issue,
-                                          const TileSrc& dsrc, int dkt) {
-  constexpr int kFirst = kLast ? kDmaPerWave : kSplitFirst;
-  constexpr int kRest = kDmaPerWave - kSplitFirst;
+// register set 0, the next k-tile's activations in flight into the other
+// stage (its weights already there). Fragment reads run one MFMA k-step ahead
+// (the scheduling barriers keep the compiler from sinking each read next to
+// its use). Before the last k-step's MFMAs the wave waits for its activation
+// DMA of the next k-tile (the weight loads issued after it, and the previous
+// tile's kStores output stores if `after_stores`, may stay in flight), drains its LDS traffic, meets the other waves and reads the next
+// k-tile's first fragments; the last k-step's MFMAs carry stage S's refill.
+template <int S, bool kSwiglu, int kStores>
+__device__ __forceinline__ void ring_step(Frags& f, const Geo& g, Regs& r, bool after_stores,
+                                          const TileSrc& ds, int dkt, const TileSrc& ls, int lkt) {
   read_frags<S, 1, kSwiglu>(f, g, 1);
   __builtin_amdgcn_sched_barrier(0);
-  mma_dma<0, 1 - S, kRest>(f, pend, g, psrc, pkt, kSplitFirst);
+  mma<0>(f);
   __builtin_amdgcn_sched_barrier(0);
   read_frags<S, 0, kSwiglu>(f, g, 2);
   __builtin_amdgcn_sched_barrier(0);
@@ -263,20 +277,19 @@ __device__ __forceinline__ void ring_step(Frags& f, const Geo& g, bool has_next_
   __builtin_amdgcn_sched_barrier(0);
   mma<0>(f);
   __builtin_amdgcn_sched_barrier(0);
-  // the next k-tile's DMA is the only one in flight: vmcnt(0)
-  if (has_next_kt) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, true));
-  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(63, true));   // LDS reads only
+  if (after_stores) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPieces + kStores, true));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPieces, true));
   lds_barrier();
-  if (has_next_kt) read_frags<1 - S, 0, kSwiglu>(f, g, 0);
-  __builtin_amdgcn_sched_barrier(0);        // fragment reads before the refill
-  mma_dma<1, S, kFirst>(f, issue, g, dsrc, dkt, 0);
+  read_frags<1 - S, 0, kSwiglu>(f, g, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  mma_io<1, S>(f, r, g, ds, dkt, ls, lkt);
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // Tile L of the order: groups of kGroupM m-tiles x all n-tiles, m fastest.
 // cnt_s / off_s: the experts' counts and segment offsets, copied to LDS so
 // that per-tile lookups are LDS reads, not vector loads (whose waits would
-// also wait for the DMA in flight).
+// also wait for the loads in flight).
 template <int kOutCols>
 __device__ __forceinline__ TileInfo tile_info(const GemmArgs& a, const int* pre, const int* cnt_s,
                                               const int* off_s, int total_m, int NT, int L) {
@@ -297,39 +310,41 @@ __device__ __forceinline__ TileInfo tile_info(const GemmArgs& a, const int* pre,
   return t;
 }
 
-// DMA source of a tile for this wave. Every DMA address is in bounds by
+// Operand sources of a tile for this wave. Every address is in bounds by
 // construction: the A buffers (Xe, h) carry BM spare rows past R_cap, so a
 // tile may read BM rows from any segment start (rows past the segment only
 // feed discarded outputs), and a tile's weight rows never pass the expert's
 // 2I (or H) rows because I is a multiple of BN / 2 and H of BN. Row offsets
-// go in the scalar offset, so a lane keeps one offset register.
+// of the pieces go in the scalar offset, so a lane keeps one offset register
+// per operand.
 template <bool kSwiglu>
 __device__ __forceinline__ TileSrc tile_src(const GemmArgs& a, const TileInfo& t, int I,
                                             int wave, int ln) {
   const int Kd = a.Kd;
   const int64_t Nb = kSwiglu ? 2 * static_cast<int64_t>(I) : a.Nc;
   TileSrc s;
-  const bool b_side = wave >> 1;
-  if (!b_side) {
-    const uint64_t left = (static_cast<uint64_t>(a.a_rows) - t.row0) * Kd * 2;
-    s.rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(t.row0) * Kd),
-        0, static_cast<int>(left < 0xffffffffull ? left : 0xffffffffull), kBufferFlags);
-  } else {
-    const uint64_t size = static_cast<uint64_t>(Nb) * Kd * 2;
-    s.rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(t.e) * Nb * Kd),
-        0, static_cast<int>(size < 0xffffffffull ? size : 0xffffffffull), kBufferFlags);
-  }
-  // this wave's 128 rows of its operand
-  int row0;
-  if (!b_side) row0 = (wave & 1) * (BM / 2);
-  else if (kSwiglu) row0 = (wave & 1) ? I + t.n0 : t.n0;          // gate | up
-  else row0 = t.n0 + (wave & 1) * (BN / 2);
-  // DMA j writes 1 KiB = 8 rows x 8 chunks: lane -> (row lane / 8, physical
-  // chunk lane % 8), fetching logical chunk (lane % 8) ^ (row % 8).
+  const uint64_t left = (static_cast<uint64_t>(a.a_rows) - t.row0) * Kd * 2;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(t.row0) * Kd),
+      0, static_cast<int>(left < 0xffffffffull ? left : 0xffffffffull), kBufferFlags);
+  const uint64_t size = static_cast<uint64_t>(Nb) * Kd * 2;
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(t.e) * Nb * Kd),
+      0, static_cast<int>(size < 0xffffffffull ? size : 0xffffffffull), kBufferFlags);
+  // this wave's 64 rows of each operand's stage rows
+  const int a_row = wave * 64;
+  int b_row;
+  if (kSwiglu) b_row = wave < 2 ? t.n0 + wave * 64 : I + t.n0 + (wave - 2) * 64;  // gate | up
+  else b_row = t.n0 + wave * 64;
+  // piece j holds 8 rows x 8 chunks: lane -> (row lane / 8, physical chunk
+  // lane % 8), fetching logical chunk (lane % 8) ^ (row % 8).
   const int chunk = (ln & 7) ^ (ln >> 3);
-  s.voff = (static_cast<uint32_t>(row0 + (ln >> 3)) * Kd + chunk * 8) * 2;
+  const uint32_t a_voff = (static_cast<uint32_t>(a_row + (ln >> 3)) * Kd + chunk * 8) * 2;
+  const uint32_t b_voff = (static_cast<uint32_t>(b_row + (ln >> 3)) * Kd + chunk * 8) * 2;
+  s.d_rsrc = kRegActs ? b_rsrc : a_rsrc;
+  s.d_voff = kRegActs ? b_voff : a_voff;
+  s.r_rsrc = kRegActs ? a_rsrc : b_rsrc;
+  s.r_voff = kRegActs ? a_voff : b_voff;
   s.stride = 8u * Kd * 2;
   return s;
 }
@@ -360,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int nk = a.Kd / BK;                 // even: H % 256 == 0, I % 128 == 0
+  const int nk = a.Kd / BK;                 // even and >= 2: H % 256 == 0, I % 128 == 0
   uint16_t* __restrict__ Cb = static_cast<uint16_t*>(a.C);
 
   // XCD-aware order: blocks are dealt round-robin to the 8 XCDs; give each
@@ -371,43 +386,81 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   if (pos >= total) return;
 
   Geo g;
-  g.dma_dst = (wave >> 1) * kRegion + (wave & 1) * (BM / 2) * kCpr;
+  g.d_dst = wave * 64 * kCpr;
+  g.r_dst = wave * 64 * kCpr + lane;
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s)
     g.frag_ch[s] = (lane & 31) * kCpr + ((2 * s + (lane >> 5)) ^ (lane & 7));
   g.a_frag = wm * 128 * kCpr;
-  g.b_frag = kRegion + (kSwiglu ? wn * 64 : wn * 128) * kCpr;
+  g.b_frag = (kSwiglu ? wn * 64 : wn * 128) * kCpr;
 
   // Output geometry: acc[i][j][4 q' + q] is row (lane & 31) of row block i and
   // column 8 q' + 4 (lane / 32) + q of weight block j; after pairing lanes l
   // and l + 32 a lane holds 8 consecutive columns of one row.
   constexpr int kStores = 4 * (kSwiglu ? 2 : 4) * 2;   // 16-byte stores per lane per tile
+  static_assert(kPieces + kStores <= 63, "vmcnt range");
 
+  // The k-tile sequence runs through this block's tiles; the refills fetch
+  // from this tile (s0) or the next two (s1, s2; two ahead only when
+  // nk == 2). Past the block's last tile they re-read that tile: in bounds,
+  // never used.
+  const int last = pos + ((total - 1 - pos) / G) * G;
+  auto src_of = [&](int L) {
+    return tile_src<kSwiglu>(a, tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, min(L, last)),
+                             I, wave, lane);
+  };
   TileInfo t = tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, pos);
-  TileSrc cur = tile_src<kSwiglu>(a, t, I, wave, lane);
-  issue_stage<0>(g, cur, 0);
-  issue_stage<1>(g, cur, 1);
-  bool first = true;
-  Frags f;
-
-  for (int L = pos; L < total; L += G) {
-    const int Ln = L + G;
-    const bool has_next = Ln < total;
-    TileInfo tn = t;
-    TileSrc nxt = cur;
-    if (has_next) {
-      tn = tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, Ln);
-      nxt = tile_src<kSwiglu>(a, tn, I, wave, lane);
+  TileSrc s0 = tile_src<kSwiglu>(a, t, I, wave, lane);
+  TileSrc s1 = src_of(pos + G), s2 = src_of(pos + 2 * G);
+  // k-tile q of the sequence starting at the current tile, q < 2 nk + 2
+  auto pick = [&](int q, int& kq) -> TileSrc {
+    if (q < nk) {
+      kq = q;
+      return s0;
     }
+    if (q < 2 * nk) {
+      kq = q - nk;
+      return s1;
+    }
+    kq = q - 2 * nk;
+    return s2;
+  };
 
-    // k-tile 0 of this tile: issued before DMA(1) and, after the first tile,
-    // before the previous tile's output stores.
-    if (first) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave, false));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kDmaPerWave + kStores, false));
-    static_assert(kDmaPerWave + kStores <= 63, "vmcnt range");
-    first = false;
+  Regs r0, r1;
+  {
+    int k0, k1, k2, k3;
+    const TileSrc q0 = pick(0, k0), q1 = pick(1, k1), q2 = pick(2, k2), q3 = pick(3, k3);
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) dma_a<0>(g, q0, k0, j);
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) dma_a<1>(g, q1, k1, j);
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) r0.v[j] = load_b(q0, k0, j);
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) r1.v[j] = load_b(q1, k1, j);
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      write_b<0>(g, r0.v[j], j);
+      r0.v[j] = load_b(q2, k2, j);
+      __builtin_amdgcn_sched_barrier(0);   // write before reload
+    }
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      write_b<1>(g, r1.v[j], j);
+      r1.v[j] = load_b(q3, k3, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the activation DMAs of k-tiles 0 and 1 (the weight loads after them
+    // may stay in flight)
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPieces, true));
     lds_barrier();
-    read_frags<0, 0, kSwiglu>(f, g, 0);
+  }
+  Frags f;
+  read_frags<0, 0, kSwiglu>(f, g, 0);
+
+  bool first = true;
+#pragma clang loop unroll(disable)
+  for (int L = pos; L < total; L += G) {
     {
       // Accumulators start at zero through an MFMA with zero operands: the
       // result lands in accumulation registers directly.
@@ -423,20 +476,36 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
           f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf, zf, floatx16{}, 0, 0, 0);
     }
 
-    // Two LDS stages: k-tile kt+1 streams in while k-tile kt is multiplied.
-    // The last two k-steps already request the next tile's first k-tiles.
-    // Step kt refills its stage with k-tile kt + 2 (of the next tile past the
-    // end) and finishes the refill that step kt - 1 began.
-    constexpr bool kSplit = kSplitFirst < kDmaPerWave;
-    ring_step<0, kSwiglu, false>(f, g, true, false, cur, 0, nk > 2 || has_next,
-                                 nk > 2 ? cur : nxt, nk > 2 ? 2 : 0);
-    if (nk > 2) ring_step<1, kSwiglu, false>(f, g, true, kSplit, cur, 2, true, cur, 3);
-    for (int kt = 2; kt < nk - 2; kt += 2) {
-      ring_step<0, kSwiglu, false>(f, g, true, kSplit, cur, kt + 1, true, cur, kt + 2);
-      ring_step<1, kSwiglu, false>(f, g, true, kSplit, cur, kt + 2, true, cur, kt + 3);
-    }
-    if (nk > 2) ring_step<0, kSwiglu, false>(f, g, true, kSplit, cur, nk - 1, has_next, nxt, 0);
-    ring_step<1, kSwiglu, true>(f, g, false, kSplit && has_next, nxt, 0, has_next, nxt, 1);
+    // Stages alternate with the k-tile's parity (nk is even). Step kt waits
+    // for the activations of k-tile kt + 1 (issued one step earlier; after the
+    // previous tile's output stores for kt == 0) and refills its stage with
+    // k-tile kt + 2, loading k-tile kt + 4 into the freed registers.
+    // (a do-while: nk >= 2, and no zero-trip path for the accumulators; not
+    // peeled or unrolled, so there is one copy of the step code)
+    bool after_stores = !first;
+    first = false;
+    int kt = 0;
+#pragma clang loop unroll(disable)
+    do {
+      int dk, lk;
+      {
+        const TileSrc d = pick(kt + 2, dk), l = pick(kt + 4, lk);
+        ring_step<0, kSwiglu, kStores>(f, g, r0, after_stores, d, dk, l, lk);
+      }
+      after_stores = false;
+      {
+        const TileSrc d = pick(kt + 3, dk), l = pick(kt + 5, lk);
+        ring_step<1, kSwiglu, kStores>(f, g, r1, false, d, dk, l, lk);
+      }
+      kt += 2;
+    } while (kt < nk);
+
+    // The accumulators stay in accumulation registers up to their block's
+    // turn in the epilogue.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(f.acc[i][j]));
 
     // Epilogue: bf16 (SwiGLU for the up projection) straight to global memory
     // with buffer stores whose range check drops rows past the segment.
@@ -449,6 +518,17 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
       const uint32_t row_off = static_cast<uint32_t>(wm * 128 + i * 32 + (lane & 31)) * a.Nc;
 #pragma unroll
       for (int j = 0; j < (kSwiglu ? 2 : 4); ++j) {
+        // Copy this block's accumulators to ordinary registers here and only
+        // here (the empty asm pins the copy), so that the compiler does not
+        // move the whole tile's accumulators out at once while the register
+        // stages are live.
+        floatx16 xg = f.acc[i][j];
+        asm volatile("" : "+v"(xg));
+        floatx16 xu = xg;
+        if (kSwiglu) {
+          xu = f.acc[i][j + 2];
+          asm volatile("" : "+v"(xu));
+        }
         uint32_t d[4][2];   // [column group q'][pair]: bf16 pairs of 4 columns
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
@@ -457,11 +537,11 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
             const int v0 = 4 * qq + 2 * h2, v1 = v0 + 1;
             float x0, x1;
             if (kSwiglu) {
-              x0 = silu_mul(f.acc[i][j][v0], f.acc[i][j + 2][v0]);
-              x1 = silu_mul(f.acc[i][j][v1], f.acc[i][j + 2][v1]);
+              x0 = silu_mul(xg[v0], xu[v0]);
+              x1 = silu_mul(xg[v1], xu[v1]);
             } else {
-              x0 = f.acc[i][j][v0];
-              x1 = f.acc[i][j][v1];
+              x0 = xg[v0];
+              x1 = xg[v1];
             }
             d[qq][h2] = pack_bf16x2(x0, x1);
           }
@@ -476,12 +556,16 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
           const uint32_t col = colj + 8 * (qq + hi);
           __builtin_amdgcn_raw_buffer_store_b128(out, rC, (row_off + col) * 2, 0, 0);
         }
+        // one weight block at a time: the register stages stay live here
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    t = tn;
-    cur = nxt;
+    if (L + G < total) t = tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, L + G);
+    s0 = s1;
+    s1 = s2;
+    s2 = src_of(L + 3 * G);
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, true));   // loads and DMA past the last tile
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
