@@ -117,7 +117,10 @@ __host__ __device__ constexpr int waitcnt_vm(int n, bool lgkm0) {
 }
 
 // Row r of a stage keeps its logical 16-byte chunk c at physical chunk
-// c ^ (r & 7): the 8 rows one LDS cycle serves hit 8 distinct bank groups.
+// c ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1). gfx950's LDS has 64 banks: a
+// 16-byte fragment read serves 16 lanes (16 rows) per cycle, rows r and r + 1
+// land in opposite bank halves, and f is distinct over the 8 even rows and
+// over the 8 odd rows of any 16, so the reads are conflict-free.
 
 // Workgroup barrier that orders LDS accesses for the compiler only. It does
 // not wait for in-flight LDS DMA (callers wait with vmcnt first).
@@ -159,6 +162,7 @@ constexpr bool kRegActs = false;   // weights through registers, activations by 
 struct TileSrc {
   __amdgpu_buffer_rsrc_t d_rsrc, r_rsrc;   // DMA operand, register operand
   uint32_t d_voff, r_voff;  // this lane's byte offset of piece 0 of k-tile 0
+  uint32_t d_voff1, r_voff1;  // the same for piece 1 (odd pieces)
   uint32_t stride;          // bytes between pieces j and j + 1 (8 rows)
 };
 
@@ -218,12 +222,12 @@ __device__ __forceinline__ u32x4* reg_stage() { return kRegActs ? stage_a<S>() :
 template <int S>
 __device__ __forceinline__ void dma_a(const Geo& g, const TileSrc& s, int kt, int j) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      s.d_rsrc, (lds_void*)(dma_stage<S>() + g.d_dst + j * 8 * kCpr), 16, s.d_voff,
+      s.d_rsrc, (lds_void*)(dma_stage<S>() + g.d_dst + j * 8 * kCpr), 16, (j & 1) ? s.d_voff1 : s.d_voff,
       kt * BK * 2 + j * s.stride, 0, 0);
 }
 
 __device__ __forceinline__ u32x4 load_b(const TileSrc& s, int kt, int j) {
-  return __builtin_amdgcn_raw_buffer_load_b128(s.r_rsrc, s.r_voff, kt * BK * 2 + j * s.stride, 0);
+  return __builtin_amdgcn_raw_buffer_load_b128(s.r_rsrc, (j & 1) ? s.r_voff1 : s.r_voff, kt * BK * 2 + j * s.stride, 0);
 }
 
 template <int S>
@@ -337,7 +341,8 @@ __device__ __forceinline__ TileSrc tile_src(const GemmArgs& a, const TileInfo& t
   if (kSwiglu) b_row = wave < 2 ? t.n0 + wave * 64 : I + t.n0 + (wave - 2) * 64;  // gate | up
   else b_row = t.n0 + wave * 64;
   // piece j holds 8 rows x 8 chunks: lane -> (row lane / 8, physical chunk
-  // lane % 8), fetching logical chunk (lane % 8) ^ (row % 8).
+  // lane % 8), fetching logical chunk (lane % 8) ^ f(row); f(row) is
+  // (lane / 8) ^ (j & 1), so odd pieces use a second lane offset.
   const int chunk = (ln & 7) ^ (ln >> 3);
   const uint32_t a_voff = (static_cast<uint32_t>(a_row + (ln >> 3)) * Kd + chunk * 8) * 2;
   const uint32_t b_voff = (static_cast<uint32_t>(b_row + (ln >> 3)) * Kd + chunk * 8) * 2;
@@ -346,6 +351,13 @@ __device__ __forceinline__ TileSrc tile_src(const GemmArgs& a, const TileInfo& t
   s.r_rsrc = kRegActs ? a_rsrc : b_rsrc;
   s.r_voff = kRegActs ? a_voff : b_voff;
   s.stride = 8u * Kd * 2;
+  {
+    const int c1 = chunk ^ 1;
+    const uint32_t a1 = (static_cast<uint32_t>(a_row + (ln >> 3)) * Kd + c1 * 8) * 2;
+    const uint32_t b1 = (static_cast<uint32_t>(b_row + (ln >> 3)) * Kd + c1 * 8) * 2;
+    s.d_voff1 = kRegActs ? b1 : a1;
+    s.r_voff1 = kRegActs ? a1 : b1;
+  }
   return s;
 }
 
@@ -390,7 +402,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   g.r_dst = wave * 64 * kCpr + lane;
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s)
-    g.frag_ch[s] = (lane & 31) * kCpr + ((2 * s + (lane >> 5)) ^ (lane & 7));
+    g.frag_ch[s] = (lane & 31) * kCpr + ((2 * s + (lane >> 5)) ^ ((lane & 7) ^ ((lane >> 3) & 1)));
   g.a_frag = wm * 128 * kCpr;
   g.b_frag = (kSwiglu ? wn * 64 : wn * 128) * kCpr;
 
