@@ -644,17 +644,18 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
       floatx4 acc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
       int kb = kb0;
       for (; kb + kStreamU <= kb1; kb += kStreamU) {
-        // lane group g reads 8*kStreamU contiguous k; step j of the group
-        // pairs the j-th 8-element piece of every lane in both operands
-        const int k = kb * 32 + g * 8 * kStreamU;
+        // MFMA j takes k-block kb + j: lane group g holds its 8 elements
+        // g * 8 .. g * 8 + 7, so one load instruction reads 64 contiguous
+        // bytes of each of 16 rows (4 lanes per row)
+        const int k = kb * 32 + g * 8;
         u32x4 wa[kStreamU], xb[2][kStreamU];
 #pragma unroll
-        for (int j = 0; j < kStreamU; ++j) wa[j] = *reinterpret_cast<const u32x4*>(wp + k + j * 8);
+        for (int j = 0; j < kStreamU; ++j) wa[j] = *reinterpret_cast<const u32x4*>(wp + k + j * 32);
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
           for (int j = 0; j < kStreamU; ++j)
-            xb[q][j] = xv[q] ? *reinterpret_cast<const u32x4*>(xp[q] + k + j * 8)
+            xb[q][j] = xv[q] ? *reinterpret_cast<const u32x4*>(xp[q] + k + j * 32)
                              : u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < kStreamU; ++j)
