@@ -49,6 +49,9 @@ def _load():
     lib.oracle_combine.restype = None
     lib.oracle_combine.argtypes = [C.c_int64, C.c_int32, C.c_int64, C.c_int32, _i32p,
                                    C.c_void_p, C.c_void_p, _f64p]
+    lib.oracle_combine_epilogue.restype = None
+    lib.oracle_combine_epilogue.argtypes = [C.c_int64, C.c_int32, C.c_int64, C.c_int32, _i32p,
+                                            C.c_void_p, _f64p]
     lib.oracle_forward.restype = None
     lib.oracle_forward.argtypes = [C.c_int64, C.c_int32, C.c_int64, C.c_int32, C.c_int64,
                                    C.c_int64, C.c_int32, C.c_void_p, _i64p, C.c_void_p,
@@ -151,6 +154,20 @@ def combine(row_map: np.ndarray, weights: Optional[np.ndarray], O: np.ndarray) -
     w = None if weights is None else np.ascontiguousarray(weights, dtype=np.float32)
     y = np.empty((T, H), np.float64)
     _load().oracle_combine(T, K, H, dt, row_map.reshape(-1), _ptr(w), _ptr(O), y)
+    return y
+
+
+def combine_epilogue(src: np.ndarray, recv: np.ndarray) -> np.ndarray:
+    """Cross-rank epilogue: y[t] = sum over j of recv[src[t][j]] (src >= 0), double."""
+    src = np.ascontiguousarray(src, dtype=np.int32)
+    T, J = src.shape
+    recv = np.ascontiguousarray(recv)
+    dt = _dtype_code(recv)
+    H = recv.shape[1]
+    if src.size and src.max() >= recv.shape[0]:
+        raise ValueError("src points past the received rows")
+    y = np.empty((T, H), np.float64)
+    _load().oracle_combine_epilogue(T, J, H, dt, src.reshape(-1), _ptr(recv), y)
     return y
 
 

@@ -159,6 +159,19 @@ void oracle_combine(int64_t T, int32_t K, int64_t H, int32_t dtype,
     }
 }
 
+void oracle_combine_epilogue(int64_t T, int32_t J, int64_t H, int32_t dtype,
+                             const int32_t* src, const void* recv, double* y) {
+    for (int64_t t = 0; t < T; ++t) {
+        double* yt = y + t * H;
+        for (int64_t h = 0; h < H; ++h) yt[h] = 0.0;
+        for (int32_t j = 0; j < J; ++j) {
+            const int32_t row = src[t * J + j];
+            if (row < 0) continue;
+            for (int64_t h = 0; h < H; ++h) yt[h] += elem(recv, dtype, (int64_t)row * H + h);
+        }
+    }
+}
+
 void oracle_forward(int64_t T, int32_t K, int64_t expert_begin, int32_t E,
                     int64_t H, int64_t I, int32_t dtype, const void* x,
                     const int64_t* idx, const float* w, const void* w1,

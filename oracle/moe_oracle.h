@@ -64,6 +64,16 @@ void oracle_combine(int64_t T, int32_t K, int64_t H, int32_t dtype,
                     const int32_t* row_map, const float* w, const void* O,
                     double* y);
 
+/* Cross-rank combine epilogue (DeepEP issue #760, body: the epilogue sums,
+ * for each output token, the rows returned by the ranks that hold its
+ * experts; repro: combine without weights, so a token's result is the plain
+ * sum of what it gets back). recv [N, H] of `dtype`; src [T, J]: src[t][j] is
+ * the recv row of contribution j of token t, or -1 for none.
+ *   y[t] = sum over j ascending with src[t][j] >= 0 of recv[src[t][j]]
+ * y [T, H] double; a token with no contribution is 0. */
+void oracle_combine_epilogue(int64_t T, int32_t J, int64_t H, int32_t dtype,
+                             const int32_t* src, const void* recv, double* y);
+
 /* Whole layer for the listed tokens (tokens == NULL: all T, in order).
  * y [n_tokens, H] double. Weights of non-local slots are never read. */
 void oracle_forward(int64_t T, int32_t K, int64_t expert_begin, int32_t E,

@@ -347,6 +347,66 @@ def test_deepep760_combine_only_emulated(oracle_mod):
     assert np.all(combined[~real] == g["expected_pad"])
 
 
+def test_deepep760_cross_rank_epilogue(oracle_mod):
+    """The same repro with the cross-rank sum done by the epilogue oracle:
+    the 32 rank partials are stacked into one receive buffer and every output
+    token lists the rows of all ranks; the result must be the repro's
+    expected 1 on real rows and 0 on padding rows, and must equal the plain
+    sum of the partials."""
+    g = load_golden("deepep760_combine_only.txt")
+    W, tp, topk, E = g["world_size"], g["tp_size"], g["topk"], g["local_experts"]
+    idx = -np.ones((W, topk), np.int64)
+    w = np.zeros((W, topk), np.float32)
+    real = np.array([r % tp == 0 for r in range(W)])
+    idx[real] = np.arange(topk) * E
+    w[real] = g["topk_weight"]
+    H = 8
+    partials = np.zeros((W, W, H), np.float32)       # [source rank, token, H]
+    for rank in range(W):
+        r = oracle_mod.route(idx, E, expert_begin=rank * E)
+        if r["R"]:
+            partials[rank] = oracle_mod.combine(r["row_map"], w, np.ones((r["R"], H), np.float32))
+    recv = partials.reshape(W * W, H)
+    src = (np.arange(W)[None, :] * W + np.arange(W)[:, None]).astype(np.int32)   # [token, rank]
+    y = oracle_mod.combine_epilogue(src, recv)
+    assert np.all(y[real] == g["expected_real"])
+    assert np.all(y[~real] == g["expected_pad"])
+    assert np.array_equal(y, partials.astype(np.float64).sum(axis=0))
+
+
+def test_epilogue_one_hot_is_a_copy(oracle_mod):
+    """One contribution per token (the rest -1): the output is that received
+    row, exactly, for bf16 and fp32 rows."""
+    rng = np.random.default_rng(7)
+    for dt in ("bf16", "f32"):
+        f = rng.standard_normal((20, 24)).astype(np.float32)
+        recv = gen.f32_to_bf16_bits(f) if dt == "bf16" else f
+        want = gen.bf16_bits_to_f32(recv) if dt == "bf16" else f
+        src = -np.ones((9, 5), np.int32)
+        rows = rng.integers(0, 20, 9)
+        src[np.arange(9), rng.integers(0, 5, 9)] = rows
+        y = oracle_mod.combine_epilogue(src, recv)
+        assert np.array_equal(y, want[rows].astype(np.float64))
+        assert np.all(oracle_mod.combine_epilogue(-np.ones((3, 4), np.int32), recv) == 0.0)
+
+
+def test_epilogue_equals_count_matrix_product(oracle_mod):
+    """Second formulation: y = S @ recv with S[t, r] the number of times row r
+    is listed for token t (duplicates count twice, -1 never)."""
+    rng = np.random.default_rng(11)
+    for _ in range(20):
+        N, T, J, H = rng.integers(1, 30), rng.integers(1, 12), rng.integers(1, 9), rng.integers(1, 16)
+        recv = rng.standard_normal((N, H)).astype(np.float32)
+        src = rng.integers(-1, N, (T, J)).astype(np.int32)
+        S = np.zeros((T, N))
+        for t in range(T):
+            for j in range(J):
+                if src[t, j] >= 0:
+                    S[t, src[t, j]] += 1
+        y = oracle_mod.combine_epilogue(src, recv)
+        np.testing.assert_allclose(y, S @ recv.astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
 def test_sglang6092_real_rows_in_padded_buffer():
     g = load_golden("sglang6092_dp_batch.txt")
     wl = gen.make_workload("c4")

@@ -25,6 +25,10 @@ MUTANTS = {
     "combine_unweighted": ("double wk = w ? (double)w[t * K + k] : 1.0;\n            for (int64_t j = 0; j < H; ++j) yt[j] += wk * elem(",
                            "double wk = 1.0;\n            for (int64_t j = 0; j < H; ++j) yt[j] += wk * elem("),
     "bf16_widen": ("uint32_t u = (uint32_t)b << 16;", "uint32_t u = (uint32_t)b << 15;"),
+    "epilogue_stops_at_gap": ("            if (row < 0) continue;\n            for (int64_t h = 0; h < H; ++h) yt[h] += elem(recv",
+                              "            if (row < 0) break;\n            for (int64_t h = 0; h < H; ++h) yt[h] += elem(recv"),
+    "epilogue_first_only": ("for (int32_t j = 0; j < J; ++j) {\n            const int32_t row = src[t * J + j];",
+                            "for (int32_t j = 0; j < (J > 1 ? J - 1 : J); ++j) {\n            const int32_t row = src[t * J + j];"),
 }
 
 
