@@ -156,6 +156,88 @@ def lowbatch_combine(reps: int):
     return out
 
 
+def _graph_time(launch, check, reps: int, replays: int = 5) -> float:
+    """Mean device time per launch (us) of `launch` captured `reps` times in a
+    HIP graph and replayed; `check()` must hold after the eager launch and
+    after every checked replay."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        launch(side)
+    side.synchronize()
+    if not check():
+        raise RuntimeError("eager launch failed its check")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for _ in range(reps):
+            launch(side)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        if not check():
+            raise RuntimeError("graph replay differs from the eager launch")
+    st = torch.cuda.current_stream(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(st)
+    for _ in range(replays):
+        g.replay()
+    b.record(st)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * replays) * 1e3
+
+
+def lowbatch_epilogue(reps: int):
+    """Device time of moe_combine_epilogue on the DeepEP issue #760 combine
+    shape: H=3584, 32 source ranks, one real output row in 8 with 16 rank
+    contributions (the ranks holding its 16 experts), padding rows with none;
+    and a dense variant where every output row is real. T = 1, 2, 4, 8 against
+    T = 64; graph-replayed launches (kernel plus dispatch gap)."""
+    import numpy as np
+    import torch
+
+    import top_reduce_amd as tr
+
+    dev = torch.device("cuda:0")
+    reps = max(reps, 50)
+    H, P, J = 3584, 32, 16
+    out = {"unit": "us", "launches_per_graph": reps, "hidden": H, "ranks": P,
+           "contributions_per_real_row": J}
+    rng = np.random.default_rng(760)
+    for variant in ("stride", "dense"):
+        times = {}
+        for T in (1, 2, 4, 8, 64):
+            real = np.ones(T, bool) if variant == "dense" else (np.arange(T) % 8 == 0)
+            src = -np.ones((T, P), np.int32)
+            for t in np.nonzero(real)[0]:
+                src[t, :J] = np.arange(J) * T + t          # rank j's row for token t
+            recv = torch.from_numpy(rng.standard_normal((P * T, H)).astype(np.float32)).to(
+                dev).to(torch.bfloat16)
+            src_d = torch.from_numpy(src).to(dev)
+            y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+            ref = torch.zeros((T, H), dtype=torch.float32, device=dev)
+            for t in range(T):
+                for j in range(P):
+                    if src[t, j] >= 0:
+                        ref[t] += recv[src[t, j]].float()
+            ref_bf = ref.to(torch.bfloat16)
+
+            def launch(stream, src_d=src_d, recv=recv, y=y):
+                tr.combine_epilogue(src_d, recv, y=y, stream=stream)
+
+            def check(y=y, ref_bf=ref_bf):
+                return bool(torch.equal(y.view(torch.int16), ref_bf.view(torch.int16)))
+
+            times[T] = _graph_time(launch, check, reps)
+        out[variant] = {str(T): round(t, 3) for T, t in times.items()}
+        out[variant + "_ok"] = all(times[T] <= times[64] for T in (1, 2, 4, 8))
+    log(f"[bench] low-batch epilogue (us): {out}")
+    return out
+
+
 def copy_reference(stream, nbytes: int = 1 << 30, reps: int = 20):
     """Bandwidth of a plain device copy (torch's elementwise negation, read
     nbytes + write nbytes) on the same GPU in the same run: the practical
@@ -368,6 +450,7 @@ def main():
 
     if not args.no_lowbatch:
         result["lowbatch_combine"] = lowbatch_combine(args.steps)
+        result["lowbatch_epilogue"] = lowbatch_epilogue(args.steps)
     result["hbm_copy_reference"] = copy_reference(stream)
 
     # Sampled parity and the CPU oracle baseline on a bounded sample.

@@ -48,7 +48,7 @@
 extern "C" {
 #endif
 
-#define TR_ABI_VERSION 1
+#define TR_ABI_VERSION 2
 
 typedef enum {
     TR_OK = 0,
@@ -157,6 +157,23 @@ tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStre
  * occupy many compute units. */
 tr_status moe_combine_reduce(const tr_moe_plan* plan, const void* expert_out,
                              const float* topk_weights, void* y, hipStream_t stream);
+
+/* Cross-rank combine epilogue (DeepEP issue #760, body: after combine's
+ * all-to-all, every output token sums the rows returned by the ranks that
+ * hold its experts; the repro's combine takes no weights). Standalone: no
+ * plan.
+ *   y[t] = sum over j ascending with 0 <= src[t][j] < n_recv of recv[src[t][j]]
+ * accumulated in fp32 and rounded once to dtype; a token with no
+ * contribution is +0. recv: device [n_recv, H] rows of dtype (e.g. the P
+ * ranks' partial rows one after the other); src: device int32 [T, J], -1 for
+ * no contribution (indices >= n_recv count as none); y: device [T, H], must
+ * not overlap recv. The hidden dimension is split across wavefronts (512
+ * elements each), so a handful of tokens still occupies many compute units.
+ * Shapes: 1 <= J <= 65536, H a multiple of 8; T == 0 is a no-op. recv and y
+ * 16-byte aligned, src 4-byte aligned. */
+tr_status moe_combine_epilogue(int64_t T, int32_t J, int64_t H, tr_dtype dtype,
+                               const int32_t* src, const void* recv, int64_t n_recv, void* y,
+                               hipStream_t stream);
 
 /* Copies stats to host_out[4] = {R, rows with a local route, ignored slots,
  * empty experts} and synchronises `stream` (opt-in host sync, the counterpart

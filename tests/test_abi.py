@@ -25,7 +25,8 @@ def _declared():
 def test_header_declares_entry_points():
     names = _declared()
     for n in ("moe_workspace_size", "moe_plan", "moe_forward", "moe_expand", "moe_grouped_gemm",
-              "moe_combine_reduce", "moe_plan_stats", "moe_grouped_gemm_up", "moe_grouped_gemm_down", "moe_last_error", "moe_abi_version"):
+              "moe_combine_reduce", "moe_plan_stats", "moe_grouped_gemm_up", "moe_grouped_gemm_down",
+              "moe_combine_epilogue", "moe_last_error", "moe_abi_version"):
         assert n in names
 
 
@@ -127,6 +128,27 @@ def test_forward_rejects_misaligned_buffers():
     assert lib.moe_forward(C.byref(st), mis, None, ok, ok, ok, None) == -1
     assert b"aligned" in lib.moe_last_error()
     assert lib.moe_forward(C.byref(st), ok, None, None, ok, ok, None) == -1
+
+
+def test_combine_epilogue_checks_arguments_on_the_host():
+    """Every bad argument is rejected before any launch (no GPU needed);
+    T == 0 is a no-op that touches no pointer."""
+    lib = tr.load_library()
+    ok = C.c_void_p(1 << 41)
+    src = C.c_void_p(1 << 42)
+    bf16 = B.BF16
+    assert lib.moe_combine_epilogue(0, 4, 256, bf16, None, None, 0, None, None) == 0
+    assert lib.moe_combine_epilogue(-1, 4, 256, bf16, src, ok, 8, ok, None) == -1
+    assert lib.moe_combine_epilogue(2, 0, 256, bf16, src, ok, 8, ok, None) == -1
+    assert lib.moe_combine_epilogue(2, 70000, 256, bf16, src, ok, 8, ok, None) == -1
+    assert lib.moe_combine_epilogue(2, 4, 12, bf16, src, ok, 8, ok, None) == -2
+    assert b"multiple of 8" in lib.moe_last_error()
+    assert lib.moe_combine_epilogue(2, 4, 256, 9, src, ok, 8, ok, None) == -1
+    assert lib.moe_combine_epilogue(2, 4, 256, bf16, None, ok, 8, ok, None) == -1
+    assert lib.moe_combine_epilogue(2, 4, 256, bf16, src, ok, 8, None, None) == -1
+    assert lib.moe_combine_epilogue(2, 4, 256, bf16, src, C.c_void_p((1 << 41) + 8), 8, ok, None) == -1
+    assert b"aligned" in lib.moe_last_error()
+    assert lib.moe_combine_epilogue(2, 4, 256, bf16, src, ok, -1, ok, None) == -1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     FLAG_GEMM_FORCE_TILED,
     MoePlan,
     TopReduceError,
+    combine_epilogue,
     combine_reduce,
     expand,
     forward,

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libtopreduce.so"
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 BF16, F32 = 0, 1
 IDX_I32, IDX_I64 = 0, 1
 FLAG_GEMM_FORCE_TILED = 0x1
@@ -82,6 +82,9 @@ def load_library():
     lib.moe_grouped_gemm_down.argtypes = [C.POINTER(PlanStruct), vp, vp]
     lib.moe_combine_reduce.restype = st
     lib.moe_combine_reduce.argtypes = [C.POINTER(PlanStruct), vp, vp, vp, vp]
+    lib.moe_combine_epilogue.restype = st
+    lib.moe_combine_epilogue.argtypes = [C.c_int64, C.c_int32, C.c_int64, C.c_int32, vp, vp,
+                                         C.c_int64, vp, vp]
     lib.moe_plan_stats.restype = st
     lib.moe_plan_stats.argtypes = [C.POINTER(PlanStruct), C.POINTER(C.c_int32), vp]
     lib.moe_last_error.restype = C.c_char_p
@@ -284,6 +287,28 @@ def combine_reduce(p: MoePlan, topk_weights: Optional[torch.Tensor],
     _check(load_library().moe_combine_reduce(C.byref(p.struct), C.c_void_p(op), C.c_void_p(wp),
                                              C.c_void_p(yp or None),
                                              _stream_ptr(stream, p.ws.device)))
+    return y
+
+
+def combine_epilogue(src: torch.Tensor, recv: torch.Tensor, y: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """moe_combine_epilogue: y [T, H], y[t] = sum of recv[src[t][j]] over src[t][j] >= 0.
+    src: int32 [T, J] on the GPU; recv: [N, H] bfloat16 or float32 on the GPU."""
+    if src.dim() != 2 or src.dtype != torch.int32:
+        raise TypeError("src must be an int32 [T, J] tensor")
+    if recv.dim() != 2:
+        raise ValueError("recv must be [N, H]")
+    T, J = src.shape
+    N, H = recv.shape
+    dt = recv.dtype
+    if y is None:
+        y = torch.empty((T, H), dtype=dt, device=recv.device)
+    sp = _dev_tensor(src, "src") if T > 0 else 0
+    rp = _dev_tensor(recv, "recv", dt) if N > 0 else 0
+    yp = _dev_tensor(y, "y", dt, (T, H)) if T > 0 else 0
+    _check(load_library().moe_combine_epilogue(T, J, H, _dtype_code(dt), C.c_void_p(sp or None),
+                                               C.c_void_p(rp or None), N, C.c_void_p(yp or None),
+                                               _stream_ptr(stream, recv.device)))
     return y
 
 

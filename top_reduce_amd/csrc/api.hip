@@ -247,6 +247,25 @@ tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_
                     "moe_combine_reduce launch");
 }
 
+tr_status moe_combine_epilogue(int64_t T, int32_t J, int64_t H, tr_dtype dtype,
+                               const int32_t* src, const void* recv, int64_t n_recv, void* y,
+                               hipStream_t stream) {
+  if (T < 0) return fail(TR_EINVAL, "T must be >= 0");
+  if (J < 1 || J > 65536) return fail(TR_EINVAL, "J must be in [1, 65536]");
+  if (H < 8 || H % 8 != 0 || H > (int64_t{1} << 22))
+    return fail(TR_EUNSUPPORTED, "H must be a positive multiple of 8 (at most 2^22)");
+  if (dtype != TR_BF16 && dtype != TR_F32) return fail(TR_EINVAL, "unknown dtype");
+  if (n_recv < 0 || n_recv > INT32_MAX) return fail(TR_EINVAL, "n_recv must be in [0, 2^31)");
+  if (T * static_cast<int64_t>(J) >= (int64_t{1} << 31)) return fail(TR_EINVAL, "T * J too large");
+  if (T == 0) return ok();
+  if (!src || !aligned(src, 4)) return fail(TR_EINVAL, "src must be non-NULL and 4-byte aligned");
+  tr_status s;
+  if ((s = check_buf(y, "y", true)) != TR_OK) return s;
+  if (n_recv > 0 && (s = check_buf(recv, "recv", true)) != TR_OK) return s;
+  return hip_status(tr::combine_epilogue(T, J, H, dtype == TR_BF16, src, recv, n_recv, y, stream),
+                    "moe_combine_epilogue launch");
+}
+
 tr_status moe_plan_stats(const tr_moe_plan* plan, int32_t* host_out, hipStream_t stream) {
   tr_status s = check_plan(plan);
   if (s != TR_OK) return s;

@@ -20,7 +20,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSlab = kWave * 8;  // elements per wave item
-constexpr int kBatch = 8;         // slots loaded before accumulating
+constexpr int kBatch = 8;         // slots loaded before accumulating (16 and 32 measured slower)
 
 template <bool kBF16>
 struct Row8;
@@ -67,11 +67,13 @@ struct Row8<false> {
   }
 };
 
+// Rows at or past n_rows count as absent, like -1.
 template <bool kBF16>
 __global__ __launch_bounds__(kThreads) void combine_rows(const void* __restrict__ O,
                                                          const int* __restrict__ row_map,
                                                          const float* __restrict__ w, int64_t T,
-                                                         int K, int64_t H, void* __restrict__ y) {
+                                                         int K, int64_t H, int64_t n_rows,
+                                                         void* __restrict__ y) {
   const int64_t nslab = (H + kSlab - 1) / kSlab;
   const int64_t items = T * nslab;
   const int lane = lane_id();
@@ -92,6 +94,7 @@ __global__ __launch_bounds__(kThreads) void combine_rows(const void* __restrict_
       for (int j = 0; j < kBatch; ++j) {
         const int k = k0 + j;
         rows[j] = k < K ? row_map[t * K + k] : -1;
+        if (rows[j] >= n_rows) rows[j] = -1;
         wk[j] = 0.0f;
         v[j].zero();
         if (rows[j] >= 0) {
@@ -112,23 +115,41 @@ __global__ __launch_bounds__(kThreads) void combine_rows(const void* __restrict_
 
 }  // namespace
 
-hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const float* w, void* y,
-                          hipStream_t st) {
-  const tr_moe_desc& d = p.d;
-  const void* O = expert_out ? expert_out : p.O;
-  const int64_t nslab = (d.H + kSlab - 1) / kSlab;
-  const int64_t waves = d.T * nslab;
+namespace {
+
+hipError_t launch_rows(bool bf16, const void* O, const int* row_map, const float* w, int64_t T,
+                       int K, int64_t H, int64_t n_rows, void* y, hipStream_t st) {
+  const int64_t nslab = (H + kSlab - 1) / kSlab;
+  const int64_t waves = T * nslab;
   int64_t blocks = cdiv(waves, kThreads / kWave);
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 32;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) return hipSuccess;
-  if (d.dtype == TR_BF16)
+  if (bf16)
     hipLaunchKernelGGL(combine_rows<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       st, O, p.row_map, w, d.T, d.K, d.H, y);
+                       st, O, row_map, w, T, K, H, n_rows, y);
   else
     hipLaunchKernelGGL(combine_rows<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       st, O, p.row_map, w, d.T, d.K, d.H, y);
+                       st, O, row_map, w, T, K, H, n_rows, y);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const float* w, void* y,
+                          hipStream_t st) {
+  const tr_moe_desc& d = p.d;
+  const void* O = expert_out ? expert_out : p.O;
+  return launch_rows(d.dtype == TR_BF16, O, p.row_map, w, d.T, d.K, d.H, p.R_cap, y, st);
+}
+
+// The cross-rank epilogue is the same reduction with unit weights over the
+// caller's index map: one wavefront per 512-element slab of an output row, so
+// a handful of tokens still spreads over many wavefronts (DeepEP issue #760,
+// the first proposed fix).
+hipError_t combine_epilogue(int64_t T, int J, int64_t H, bool bf16, const int* src,
+                            const void* recv, int64_t n_recv, void* y, hipStream_t st) {
+  return launch_rows(bf16, recv, src, nullptr, T, J, H, n_recv, y, st);
 }
 
 }  // namespace tr

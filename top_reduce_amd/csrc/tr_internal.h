@@ -27,6 +27,9 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
                         hipStream_t st);
 hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const float* w, void* y,
                           hipStream_t st);
+// y[t] = sum over j of recv[src[t][j]] (src >= 0 and < n_recv), unit weights.
+hipError_t combine_epilogue(int64_t T, int J, int64_t H, bool bf16, const int* src,
+                            const void* recv, int64_t n_recv, void* y, hipStream_t st);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
