@@ -2,9 +2,10 @@
 """Throughput of one GPU's share of the expert-parallel MoE FFN on MI355X.
 
 One step = the whole hot path on one batch: moe_plan (route scan), then the
-four kernels moe_forward runs (expand, grouped SwiGLU GEMM up and down,
-weighted top-k reduce) through their stage entry points, on synthetic inputs
-already resident in HBM. Default workload: the prefill shape
+kernels moe_forward runs (for bf16: grouped SwiGLU GEMM up gathering the
+received rows, GEMM down, weighted top-k reduce; for fp32 an expand pass
+first) through their stage entry points, on synthetic inputs already resident
+in HBM. Default workload: the prefill shape
 (16384 received tokens, H=7168, I=2048, 32 local experts of 256, top-8, Zipf
 s=1.0 popularity), bf16.
 
@@ -319,24 +320,36 @@ def main():
         log(f"[bench] copy calibration: torch.neg over {n * 2} bytes read + {n * 2} written, x3")
         del src, dst
 
-    # One step = plan (route scan) + forward (expand, grouped GEMM up and
-    # down, combine-reduce): the same kernels moe_forward launches, called
-    # stage by stage so that events between the stages, on the launch stream,
-    # give each kernel's device time inside the timed region.
-    stage_names = ("route_scan", "expand", "gemm_up", "gemm_down", "combine_reduce")
+    # One step = plan (route scan) + forward: the same kernels moe_forward
+    # launches (bf16: GEMM up gathering x through the route table, GEMM down,
+    # combine-reduce; fp32: expand, GEMM up over the expanded rows, GEMM down,
+    # combine-reduce), called stage by stage so that events between the
+    # stages, on the launch stream, give each kernel's device time inside the
+    # timed region.
+    gather = bf16 and wl.T * wl.H * 2 <= 0x7FFFFFFF
+    stage_names = (("route_scan", "gemm_up", "gemm_down", "combine_reduce") if gather else
+                   ("route_scan", "expand", "gemm_up", "gemm_down", "combine_reduce"))
 
     def staged_step(evs):
-        evs[0].record(stream)
+        i = 0
+        evs[i].record(stream)
         q = tr.plan(idx, E=wl.E, H=wl.H, I=wl.I, dtype=tdt, ws=ws, stream=stream)
-        evs[1].record(stream)
-        tr.expand(q, x, stream=stream)
-        evs[2].record(stream)
-        tr.grouped_gemm_up(q, w1, stream=stream)
-        evs[3].record(stream)
+        i += 1
+        evs[i].record(stream)
+        if gather:
+            tr.grouped_gemm_up_x(q, x, w1, stream=stream)
+        else:
+            tr.expand(q, x, stream=stream)
+            i += 1
+            evs[i].record(stream)
+            tr.grouped_gemm_up(q, w1, stream=stream)
+        i += 1
+        evs[i].record(stream)
         tr.grouped_gemm_down(q, w2, stream=stream)
-        evs[4].record(stream)
+        i += 1
+        evs[i].record(stream)
         tr.combine_reduce(q, w, y=y, stream=stream)
-        evs[5].record(stream)
+        evs[i + 1].record(stream)
 
     def new_events():
         return [torch.cuda.Event(enable_timing=True) for _ in range(len(stage_names) + 1)]
@@ -363,7 +376,7 @@ def main():
                           "ms_per_step": ms_step, "loop_only": True}), flush=True)
         return
     eager = {"ms_per_step": ms_step, "tokens_per_s": tokens_per_s,
-             "launch": "plan + the four stage entry points from Python, events between stages"}
+             "launch": "plan + the stage entry points from Python, events between stages"}
 
     # The same step (moe_plan + moe_forward) captured once in a HIP graph and
     # replayed: the host launch cost, which dominates the small decode shapes,
@@ -411,6 +424,8 @@ def main():
         "gemm_down": ("mfma" if bf16 else "alu", 2.0 * R * H * I),
         "combine_reduce": ("hbm", R * H * b + T * H * b + 8 * T * K),
     }
+    if gather:
+        del work["expand"]
     stages = {"route_scan": {"us": us["route_scan"]}}
     for k, (bound, amount) in work.items():
         t_s = us[k] / 1e6

@@ -16,7 +16,8 @@
  * The path, per call sequence:
  *   moe_plan     route scan: per-expert counts and segment offsets, and the
  *                stable maps between received slots and expanded rows
- *   moe_forward  = moe_expand + moe_grouped_gemm + moe_combine_reduce
+ *   moe_forward  = moe_expand + moe_grouped_gemm + moe_combine_reduce (bf16
+ *                runs GEMM1 straight from x instead: moe_grouped_gemm_up_x)
  *
  * Conventions for every entry point:
  *  - Pointers named "device" are HIP device (or managed) memory; the others
@@ -126,7 +127,8 @@ tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size
  * y: device [T, H], may alias x; no other aliasing. Accumulation is fp32;
  * for bf16 the intermediate h and expert outputs are rounded to bf16.
  * Equivalent to moe_expand, moe_grouped_gemm, moe_combine_reduce(plan, NULL,
- * topk_weights, y). */
+ * topk_weights, y); for bf16 it runs moe_grouped_gemm_up_x,
+ * moe_grouped_gemm_down and moe_combine_reduce, so Xe is not written. */
 tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_weights,
                       const void* w1, const void* w2, void* y, hipStream_t stream);
 
@@ -145,6 +147,13 @@ tr_status moe_grouped_gemm(const tr_moe_plan* plan, const void* w1, const void* 
  * epilogue), _down computes O from h and w2. Running _up then _down on one
  * stream is exactly moe_grouped_gemm. */
 tr_status moe_grouped_gemm_up(const tr_moe_plan* plan, const void* w1, hipStream_t stream);
+/* GEMM1 with the SwiGLU epilogue straight from the received rows: the
+ * activation tiles are gathered from x (device [T, H]) through the plan's route
+ * table, so no expand pass and no Xe are needed (the fused form of the
+ * expand step). h equals moe_expand followed by moe_grouped_gemm_up. bf16 with
+ * T * H * 2 < 2^31; otherwise it runs moe_expand and moe_grouped_gemm_up. */
+tr_status moe_grouped_gemm_up_x(const tr_moe_plan* plan, const void* x, const void* w1,
+                                hipStream_t stream);
 tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStream_t stream);
 
 /* Weighted top-k reduce (DeepEP issue #48: the reduction before the combine

@@ -26,7 +26,8 @@ def test_header_declares_entry_points():
     names = _declared()
     for n in ("moe_workspace_size", "moe_plan", "moe_forward", "moe_expand", "moe_grouped_gemm",
               "moe_combine_reduce", "moe_plan_stats", "moe_grouped_gemm_up", "moe_grouped_gemm_down",
-              "moe_combine_epilogue", "moe_last_error", "moe_abi_version"):
+              "moe_combine_epilogue", "moe_grouped_gemm_up_x", "moe_last_error",
+              "moe_abi_version"):
         assert n in names
 
 
@@ -110,6 +111,7 @@ def test_entry_points_reject_null_plan():
     assert lib.moe_expand(None, None, None) == -1
     assert lib.moe_grouped_gemm(None, None, None, None) == -1
     assert lib.moe_grouped_gemm_up(None, None, None) == -1
+    assert lib.moe_grouped_gemm_up_x(None, None, None, None) == -1
     assert lib.moe_grouped_gemm_down(None, None, None) == -1
     assert lib.moe_combine_reduce(None, None, None, None, None) == -1
     assert lib.moe_plan_stats(None, None, None) == -1

@@ -186,3 +186,46 @@ def test_error_convention_on_device():
     with pytest.raises(tr.TopReduceError) as ei:
         tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch.float32, ws=small)
     assert ei.value.status == -3
+
+
+@pytest.mark.parametrize("name,flags", [("mid", 0), ("mid", tr.FLAG_GEMM_FORCE_TILED),
+                                        ("mid", tr.FLAG_GEMM_FORCE_STREAM),
+                                        ("mid_small_experts", 0), ("mid_f32", 0), ("c1", 0)])
+def test_up_x_equals_expand_then_up(name, flags):
+    """GEMM1 gathering the received rows through the route table computes the
+    same h, bit for bit, as expand followed by GEMM1 over Xe: the same rows
+    reach the same tile positions and the arithmetic order is unchanged (fp32
+    takes the expand route inside the call)."""
+    say(f"up_x {name} flags={flags}")
+    wl = gen.make_workload(name, with_weights=True)
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch_dtype(wl), flags=flags)
+    R = oracle.route(wl.idx, wl.E)["R"]
+    v = p.views()
+    tr.expand(p, d["x"])
+    tr.grouped_gemm_up(p, d["w1"])
+    h_ref = v["h"][:R].clone()
+    v["h"][:R].zero_()
+    tr.grouped_gemm_up_x(p, d["x"], d["w1"])
+    torch.cuda.synchronize()
+    h_ref_b, h_b = host(h_ref), host(v["h"][:R])
+    assert np.array_equal(h_b.view(np.uint8), h_ref_b.view(np.uint8)), "h differs"
+
+
+@pytest.mark.parametrize("T", [1, 3, 64])
+def test_up_x_decode(T):
+    """Decode batches (weight-streaming kernel) gathering from x: h equals the
+    expand route's."""
+    say(f"up_x c3 T={T}")
+    wl = gen.make_workload("c3", T=T, variant="random", with_weights=True)
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch_dtype(wl))
+    R = oracle.route(wl.idx, wl.E)["R"]
+    v = p.views()
+    tr.expand(p, d["x"])
+    tr.grouped_gemm_up(p, d["w1"])
+    h_ref = host(v["h"][:R].clone())
+    v["h"][:R].zero_()
+    tr.grouped_gemm_up_x(p, d["x"], d["w1"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(v["h"][:R]).view(np.uint8), h_ref.view(np.uint8))

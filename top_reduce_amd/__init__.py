@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     grouped_gemm,
     grouped_gemm_down,
     grouped_gemm_up,
+    grouped_gemm_up_x,
     lib_path,
     load_library,
     make_desc,

@@ -82,6 +82,8 @@ def load_library():
     lib.moe_grouped_gemm_down.argtypes = [C.POINTER(PlanStruct), vp, vp]
     lib.moe_combine_reduce.restype = st
     lib.moe_combine_reduce.argtypes = [C.POINTER(PlanStruct), vp, vp, vp, vp]
+    lib.moe_grouped_gemm_up_x.restype = st
+    lib.moe_grouped_gemm_up_x.argtypes = [C.POINTER(PlanStruct), vp, vp, vp]
     lib.moe_combine_epilogue.restype = st
     lib.moe_combine_epilogue.argtypes = [C.c_int64, C.c_int32, C.c_int64, C.c_int32, vp, vp,
                                          C.c_int64, vp, vp]
@@ -253,6 +255,17 @@ def grouped_gemm(p: MoePlan, w1: torch.Tensor, w2: torch.Tensor, stream=None) ->
     _check(load_library().moe_grouped_gemm(C.byref(p.struct), C.c_void_p(w1p or None),
                                            C.c_void_p(w2p or None),
                                            _stream_ptr(stream, p.ws.device)))
+
+
+def grouped_gemm_up_x(p: MoePlan, x: torch.Tensor, w1: torch.Tensor, stream=None) -> None:
+    """moe_grouped_gemm_up_x: GEMM1 + SwiGLU gathering the received rows x (no Xe)."""
+    d = p.desc
+    dt = _torch_dtype(d.dtype)
+    xp = _dev_tensor(x, "x", dt, (d.T, d.H))
+    w1p = _dev_tensor(w1, "w1", dt, (d.E, 2 * d.I, d.H))
+    _check(load_library().moe_grouped_gemm_up_x(C.byref(p.struct), C.c_void_p(xp or None),
+                                                C.c_void_p(w1p or None),
+                                                _stream_ptr(stream, p.ws.device)))
 
 
 def grouped_gemm_up(p: MoePlan, w1: torch.Tensor, stream=None) -> None:

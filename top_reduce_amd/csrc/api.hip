@@ -205,6 +205,24 @@ tr_status moe_grouped_gemm_up(const tr_moe_plan* plan, const void* w1, hipStream
                     "moe_grouped_gemm_up launch");
 }
 
+tr_status moe_grouped_gemm_up_x(const tr_moe_plan* plan, const void* x, const void* w1,
+                                hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  const bool any = plan->d.T > 0;
+  if ((s = check_buf(x, "x", any)) != TR_OK) return s;
+  if ((s = check_buf(w1, "w1", any)) != TR_OK) return s;
+  if (!any) return ok();
+  if (!tr::gemm_can_gather(plan->d)) {
+    // fp32, or x past 2 GiB: expand first, then GEMM1 over Xe
+    if ((s = hip_status(tr::expand(*plan, x, stream), "moe_expand launch")) != TR_OK) return s;
+    return hip_status(tr::grouped_gemm(*plan, w1, nullptr, tr::kGemmUp, stream),
+                      "moe_grouped_gemm_up launch");
+  }
+  return hip_status(tr::grouped_gemm(*plan, w1, nullptr, tr::kGemmUp, stream, x),
+                    "moe_grouped_gemm_up_x launch");
+}
+
 tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStream_t stream) {
   tr_status s = check_plan(plan);
   if (s != TR_OK) return s;
@@ -239,10 +257,17 @@ tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_
   if ((s = check_buf(y, "y", any)) != TR_OK) return s;
   if (topk_weights && !aligned(topk_weights, 4)) return fail(TR_EINVAL, "topk_weights misaligned");
   if (!any) return ok();
-  if ((s = hip_status(tr::expand(*plan, x, stream), "moe_expand launch")) != TR_OK) return s;
-  if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream),
-                      "moe_grouped_gemm launch")) != TR_OK)
-    return s;
+  if (tr::gemm_can_gather(plan->d)) {
+    // GEMM1 reads x through the route table: no expand pass, Xe unused
+    if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream, x),
+                        "moe_grouped_gemm launch")) != TR_OK)
+      return s;
+  } else {
+    if ((s = hip_status(tr::expand(*plan, x, stream), "moe_expand launch")) != TR_OK) return s;
+    if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream),
+                        "moe_grouped_gemm launch")) != TR_OK)
+      return s;
+  }
   return hip_status(tr::combine_reduce(*plan, nullptr, topk_weights, y, stream),
                     "moe_combine_reduce launch");
 }

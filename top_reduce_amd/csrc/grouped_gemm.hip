@@ -52,7 +52,9 @@ struct GemmArgs {
   int Kd;               // reduction length
   int Nc;               // output columns
   int mode;
-  int64_t a_rows;       // rows allocated in A: R_cap + BM
+  int64_t a_rows;       // rows allocated in A: R_cap + BM (gather: the rows of x)
+  const int* gather;    // GEMM1 straight from the received rows: A row r of the
+                        // expanded order is row gather[r] of A (x); NULL: A is Xe
 };
 
 // Builds in LDS the exclusive prefix of `units(e)` over experts; returns the
@@ -156,14 +158,22 @@ __device__ __forceinline__ u32x4* stage_b() { return S == 0 ? g_b0 : g_b1; }
 // number of requests a CU keeps in flight times their L2 latency, so deeper
 // staging (both operands through registers) measured no faster.
 constexpr int kPieces = 8;
-constexpr bool kRegActs = false;   // weights through registers, activations by DMA
 
-// Where one tile's operands come from, for this wave and lane.
+// Where one tile's operands come from, for this wave and lane. Pieces are 8
+// rows apart: a lane keeps one byte offset for even and one for odd pieces
+// (the swizzle differs) and the pieces' row offsets go in the scalar offset.
+// Gathered activation rows are arbitrary, so there a lane keeps one offset per
+// activation piece.
+template <bool kGather>
 struct TileSrc {
-  __amdgpu_buffer_rsrc_t d_rsrc, r_rsrc;   // DMA operand, register operand
-  uint32_t d_voff, r_voff;  // this lane's byte offset of piece 0 of k-tile 0
-  uint32_t d_voff1, r_voff1;  // the same for piece 1 (odd pieces)
+  __amdgpu_buffer_rsrc_t d_rsrc, r_rsrc;   // activations (DMA), weights (registers)
+  uint32_t d_voff[kGather ? kPieces : 2];  // this lane's activation offsets, k-tile 0
+  uint32_t r_voff, r_voff1; // this lane's byte offset in weight piece 0 / 1, k-tile 0
   uint32_t stride;          // bytes between pieces j and j + 1 (8 rows)
+  __device__ __forceinline__ uint32_t a_voff(int j) const {
+    return kGather ? d_voff[j] : d_voff[j & 1];
+  }
+  __device__ __forceinline__ uint32_t a_soff(int j) const { return kGather ? 0u : j * stride; }
 };
 
 struct TileInfo {
@@ -214,25 +224,21 @@ __device__ __forceinline__ void mma(Frags& f) {
       f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fb[P][j], f.fa[P][i], f.acc[i][j], 0, 0, 0);
 }
 
-template <int S>
-__device__ __forceinline__ u32x4* dma_stage() { return kRegActs ? stage_b<S>() : stage_a<S>(); }
-template <int S>
-__device__ __forceinline__ u32x4* reg_stage() { return kRegActs ? stage_a<S>() : stage_b<S>(); }
-
-template <int S>
-__device__ __forceinline__ void dma_a(const Geo& g, const TileSrc& s, int kt, int j) {
+template <int S, bool G>
+__device__ __forceinline__ void dma_a(const Geo& g, const TileSrc<G>& s, int kt, int j) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      s.d_rsrc, (lds_void*)(dma_stage<S>() + g.d_dst + j * 8 * kCpr), 16, (j & 1) ? s.d_voff1 : s.d_voff,
-      kt * BK * 2 + j * s.stride, 0, 0);
+      s.d_rsrc, (lds_void*)(stage_a<S>() + g.d_dst + j * 8 * kCpr), 16, s.a_voff(j),
+      kt * BK * 2 + s.a_soff(j), 0, 0);
 }
 
-__device__ __forceinline__ u32x4 load_b(const TileSrc& s, int kt, int j) {
+template <bool G>
+__device__ __forceinline__ u32x4 load_b(const TileSrc<G>& s, int kt, int j) {
   return __builtin_amdgcn_raw_buffer_load_b128(s.r_rsrc, (j & 1) ? s.r_voff1 : s.r_voff, kt * BK * 2 + j * s.stride, 0);
 }
 
 template <int S>
 __device__ __forceinline__ void write_b(const Geo& g, const u32x4& v, int j) {
-  reg_stage<S>()[g.r_dst + j * 8 * kCpr] = v;
+  stage_b<S>()[g.r_dst + j * 8 * kCpr] = v;
 }
 
 // The 16 MFMAs of register set P with the refill of stage S between them:
@@ -241,9 +247,9 @@ __device__ __forceinline__ void write_b(const Geo& g, const u32x4& v, int j) {
 // reload of its register with k-tile `lkt` of `ls`. Spreading the issues
 // keeps the MFMA pipe fed; the compiler's per-register waits gate each LDS
 // write on its own load only.
-template <int P, int S>
-__device__ __forceinline__ void mma_io(Frags& f, Regs& r, const Geo& g, const TileSrc& ds, int dkt,
-                                       const TileSrc& ls, int lkt) {
+template <int P, int S, bool G>
+__device__ __forceinline__ void mma_io(Frags& f, Regs& r, const Geo& g, const TileSrc<G>& ds,
+                                       int dkt, const TileSrc<G>& ls, int lkt) {
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
     const int i = m >> 2, j = m & 3;
@@ -266,9 +272,10 @@ __device__ __forceinline__ void mma_io(Frags& f, Regs& r, const Geo& g, const Ti
 // DMA of the next k-tile (the weight loads issued after it, and the previous
 // tile's kStores output stores if `after_stores`, may stay in flight), drains its LDS traffic, meets the other waves and reads the next
 // k-tile's first fragments; the last k-step's MFMAs carry stage S's refill.
-template <int S, bool kSwiglu, int kStores>
+template <int S, bool kSwiglu, int kStores, bool G>
 __device__ __forceinline__ void ring_step(Frags& f, const Geo& g, Regs& r, bool after_stores,
-                                          const TileSrc& ds, int dkt, const TileSrc& ls, int lkt) {
+                                          const TileSrc<G>& ds, int dkt, const TileSrc<G>& ls,
+                                          int lkt) {
   read_frags<S, 1, kSwiglu>(f, g, 1);
   __builtin_amdgcn_sched_barrier(0);
   mma<0>(f);
@@ -317,53 +324,57 @@ __device__ __forceinline__ TileInfo tile_info(const GemmArgs& a, const int* pre,
 // Operand sources of a tile for this wave. Every address is in bounds by
 // construction: the A buffers (Xe, h) carry BM spare rows past R_cap, so a
 // tile may read BM rows from any segment start (rows past the segment only
-// feed discarded outputs), and a tile's weight rows never pass the expert's
-// 2I (or H) rows because I is a multiple of BN / 2 and H of BN. Row offsets
-// of the pieces go in the scalar offset, so a lane keeps one offset register
-// per operand.
-template <bool kSwiglu>
-__device__ __forceinline__ TileSrc tile_src(const GemmArgs& a, const TileInfo& t, int I,
-                                            int wave, int ln) {
+// feed discarded outputs); a gathered A reads row 0 of x for those rows; and
+// a tile's weight rows never pass the expert's 2I (or H) rows because I is a
+// multiple of BN / 2 and H of BN.
+template <bool kSwiglu, bool kGather>
+__device__ __forceinline__ TileSrc<kGather> tile_src(const GemmArgs& a, const TileInfo& t, int I,
+                                                     int wave, int ln) {
   const int Kd = a.Kd;
   const int64_t Nb = kSwiglu ? 2 * static_cast<int64_t>(I) : a.Nc;
-  TileSrc s;
-  const uint64_t left = (static_cast<uint64_t>(a.a_rows) - t.row0) * Kd * 2;
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(static_cast<const uint16_t*>(a.A) + static_cast<int64_t>(t.row0) * Kd),
-      0, static_cast<int>(left < 0xffffffffull ? left : 0xffffffffull), kBufferFlags);
+  TileSrc<kGather> s;
+  const uint16_t* abase = static_cast<const uint16_t*>(a.A);
+  uint64_t left = static_cast<uint64_t>(a.a_rows) * Kd * 2;
+  if (!kGather) {
+    abase += static_cast<int64_t>(t.row0) * Kd;
+    left -= static_cast<uint64_t>(t.row0) * Kd * 2;
+  }
+  s.d_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(abase), 0,
+                                               static_cast<int>(left < 0xffffffffull ? left : 0xffffffffull),
+                                               kBufferFlags);
   const uint64_t size = static_cast<uint64_t>(Nb) * Kd * 2;
-  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+  s.r_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(static_cast<const uint16_t*>(a.B) + static_cast<int64_t>(t.e) * Nb * Kd),
       0, static_cast<int>(size < 0xffffffffull ? size : 0xffffffffull), kBufferFlags);
-  // this wave's 64 rows of each operand's stage rows
-  const int a_row = wave * 64;
+  // Piece j holds 8 rows x 8 chunks: lane -> (row lane / 8, physical chunk
+  // lane % 8), fetching logical chunk (lane % 8) ^ f(row) with f(row) =
+  // (lane / 8) ^ (j & 1). This wave's activation rows are wave * 64 + j * 8 +
+  // lane / 8 of the tile; its weight rows 64 rows of the B tile.
+  const int chunk = (ln & 7) ^ (ln >> 3);
+  if (kGather) {
+#pragma unroll
+    for (int j = 0; j < kPieces; ++j) {
+      const int lr = wave * 64 + j * 8 + (ln >> 3);
+      const int row = lr < t.rows_valid ? a.gather[t.row0 + lr] : 0;
+      s.d_voff[j] = (static_cast<uint32_t>(row) * Kd + (chunk ^ (j & 1)) * 8) * 2;
+    }
+  } else {
+    const uint32_t lr = wave * 64 + (ln >> 3);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) s.d_voff[j] = (lr * Kd + (chunk ^ j) * 8) * 2;
+  }
   int b_row;
   if (kSwiglu) b_row = wave < 2 ? t.n0 + wave * 64 : I + t.n0 + (wave - 2) * 64;  // gate | up
   else b_row = t.n0 + wave * 64;
-  // piece j holds 8 rows x 8 chunks: lane -> (row lane / 8, physical chunk
-  // lane % 8), fetching logical chunk (lane % 8) ^ f(row); f(row) is
-  // (lane / 8) ^ (j & 1), so odd pieces use a second lane offset.
-  const int chunk = (ln & 7) ^ (ln >> 3);
-  const uint32_t a_voff = (static_cast<uint32_t>(a_row + (ln >> 3)) * Kd + chunk * 8) * 2;
-  const uint32_t b_voff = (static_cast<uint32_t>(b_row + (ln >> 3)) * Kd + chunk * 8) * 2;
-  s.d_rsrc = kRegActs ? b_rsrc : a_rsrc;
-  s.d_voff = kRegActs ? b_voff : a_voff;
-  s.r_rsrc = kRegActs ? a_rsrc : b_rsrc;
-  s.r_voff = kRegActs ? a_voff : b_voff;
+  s.r_voff = (static_cast<uint32_t>(b_row + (ln >> 3)) * Kd + chunk * 8) * 2;
+  s.r_voff1 = (static_cast<uint32_t>(b_row + (ln >> 3)) * Kd + (chunk ^ 1) * 8) * 2;
   s.stride = 8u * Kd * 2;
-  {
-    const int c1 = chunk ^ 1;
-    const uint32_t a1 = (static_cast<uint32_t>(a_row + (ln >> 3)) * Kd + c1 * 8) * 2;
-    const uint32_t b1 = (static_cast<uint32_t>(b_row + (ln >> 3)) * Kd + c1 * 8) * 2;
-    s.d_voff1 = kRegActs ? b1 : a1;
-    s.r_voff1 = kRegActs ? a1 : b1;
-  }
   return s;
 }
 
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <bool kSwiglu>
+template <bool kSwiglu, bool kGather>
 __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ int pre[kMaxE + 1];
@@ -418,14 +429,14 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   // never used.
   const int last = pos + ((total - 1 - pos) / G) * G;
   auto src_of = [&](int L) {
-    return tile_src<kSwiglu>(a, tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, min(L, last)),
-                             I, wave, lane);
+    return tile_src<kSwiglu, kGather>(
+        a, tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, min(L, last)), I, wave, lane);
   };
   TileInfo t = tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, pos);
-  TileSrc s0 = tile_src<kSwiglu>(a, t, I, wave, lane);
-  TileSrc s1 = src_of(pos + G), s2 = src_of(pos + 2 * G);
+  TileSrc<kGather> s0 = tile_src<kSwiglu, kGather>(a, t, I, wave, lane);
+  TileSrc<kGather> s1 = src_of(pos + G), s2 = src_of(pos + 2 * G);
   // k-tile q of the sequence starting at the current tile, q < 2 nk + 2
-  auto pick = [&](int q, int& kq) -> TileSrc {
+  auto pick = [&](int q, int& kq) -> TileSrc<kGather> {
     if (q < nk) {
       kq = q;
       return s0;
@@ -441,7 +452,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   Regs r0, r1;
   {
     int k0, k1, k2, k3;
-    const TileSrc q0 = pick(0, k0), q1 = pick(1, k1), q2 = pick(2, k2), q3 = pick(3, k3);
+    const TileSrc<kGather> q0 = pick(0, k0), q1 = pick(1, k1), q2 = pick(2, k2),
+                           q3 = pick(3, k3);
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) dma_a<0>(g, q0, k0, j);
 #pragma unroll
@@ -501,12 +513,12 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     do {
       int dk, lk;
       {
-        const TileSrc d = pick(kt + 2, dk), l = pick(kt + 4, lk);
+        const TileSrc<kGather> d = pick(kt + 2, dk), l = pick(kt + 4, lk);
         ring_step<0, kSwiglu, kStores>(f, g, r0, after_stores, d, dk, l, lk);
       }
       after_stores = false;
       {
-        const TileSrc d = pick(kt + 3, dk), l = pick(kt + 5, lk);
+        const TileSrc<kGather> d = pick(kt + 3, dk), l = pick(kt + 5, lk);
         ring_step<1, kSwiglu, kStores>(f, g, r1, false, d, dk, l, lk);
       }
       kt += 2;
@@ -639,7 +651,8 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
       for (int q = 0; q < 2; ++q) {
         const int tok = tb + q * 16 + arow;
         xv[q] = tok < cnt;
-        xp[q] = Ab + static_cast<int64_t>(off + (xv[q] ? tok : 0)) * Kd;
+        const int r = off + (xv[q] ? tok : 0);
+        xp[q] = Ab + static_cast<int64_t>(a.gather ? a.gather[r] : r) * Kd;
       }
       floatx4 acc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
       int kb = kb0;
@@ -792,8 +805,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f32(GemmArgs a, int I) {
 
 }  // namespace
 
+bool gemm_can_gather(const tr_moe_desc& d) {
+  return d.dtype == TR_BF16 && d.T * d.H * 2 <= 0x7fffffffLL;
+}
+
 hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, int parts,
-                        hipStream_t st) {
+                        hipStream_t st, const void* x_gather) {
   const tr_moe_desc& d = p.d;
   if (d.T == 0) return hipSuccess;
   const int cus = device_cu_count();
@@ -803,8 +820,16 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   const int I = static_cast<int>(d.I);
   const bool up = parts & kGemmUp, down = parts & kGemmDown;
   const int64_t a_rows = p.R_cap + kRowPad;
-  GemmArgs g1{p.Xe, w1, p.h, p.counts, p.offsets, E, static_cast<int>(d.H), I, mode, a_rows};
-  GemmArgs g2{p.h, w2, p.O, p.counts, p.offsets, E, I, static_cast<int>(d.H), mode, a_rows};
+  GemmArgs g1{p.Xe, w1, p.h, p.counts, p.offsets, E, static_cast<int>(d.H), I, mode, a_rows,
+              nullptr};
+  if (x_gather && d.dtype == TR_BF16) {
+    // GEMM1 reads the received rows through the route table: no Xe
+    g1.A = x_gather;
+    g1.a_rows = d.T;
+    g1.gather = p.row_src;
+  }
+  GemmArgs g2{p.h, w2, p.O, p.counts, p.offsets, E, I, static_cast<int>(d.H), mode, a_rows,
+              nullptr};
   hipError_t err;
 
   if (d.dtype == TR_F32) {
@@ -832,7 +857,10 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   const unsigned gs1 = static_cast<unsigned>(u1 < cus * 8 ? u1 : cus * 8);
   const unsigned gs2 = static_cast<unsigned>(u2 < cus * 8 ? u2 : cus * 8);
   if (up && mode != kModeStream) {
-    hipLaunchKernelGGL(gemm_tiled<true>, dim3(gt1), dim3(kThreads), 0, st, g1, I);
+    if (g1.gather)
+      hipLaunchKernelGGL((gemm_tiled<true, true>), dim3(gt1), dim3(kThreads), 0, st, g1, I);
+    else
+      hipLaunchKernelGGL((gemm_tiled<true, false>), dim3(gt1), dim3(kThreads), 0, st, g1, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (up && mode != kModeTiled) {
@@ -840,7 +868,7 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (down && mode != kModeStream) {
-    hipLaunchKernelGGL(gemm_tiled<false>, dim3(gt2), dim3(kThreads), 0, st, g2, I);
+    hipLaunchKernelGGL((gemm_tiled<false, false>), dim3(gt2), dim3(kThreads), 0, st, g2, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (down && mode != kModeTiled) {

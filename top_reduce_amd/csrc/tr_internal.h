@@ -22,9 +22,13 @@ hipError_t route_scan(const tr_moe_plan& p, const void* idx, hipStream_t st);
 void route_scan_geometry(int64_t T, int K, int* blocks, int* rows_per_block);
 hipError_t expand(const tr_moe_plan& p, const void* x, hipStream_t st);
 enum { kGemmUp = 1, kGemmDown = 2 };
-// parts: kGemmUp (Xe -> h, SwiGLU), kGemmDown (h -> O), or both.
+// parts: kGemmUp (Xe -> h, SwiGLU), kGemmDown (h -> O), or both. With
+// x_gather (bf16 only), GEMM1 reads the received rows x through the plan's
+// route table instead of Xe, so no expand pass is needed.
 hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, int parts,
-                        hipStream_t st);
+                        hipStream_t st, const void* x_gather = nullptr);
+// Whether GEMM1 may gather from x of this shape (32-bit buffer offsets).
+bool gemm_can_gather(const tr_moe_desc& d);
 hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const float* w, void* y,
                           hipStream_t st);
 // y[t] = sum over j of recv[src[t][j]] (src >= 0 and < n_recv), unit weights.
