@@ -371,9 +371,32 @@ def main():
     tokens_per_s = real_rows * args.steps / (ms_total / 1e3)
     log(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step (wall {wall / args.steps * 1e3:.4f}), "
         f"{tokens_per_s:.4e} tokens/s")
+    b = 2 if bf16 else 4
+    H, I, T, K = wl.H, wl.I, wl.T, wl.K
+
+    def expand_alone(reps: int = 20):
+        """moe_expand on the step's plan, outside the step: the bf16 forward
+        gathers x inside GEMM1 instead, but the entry point stays (fp32
+        forwards, callers that keep the expanded rows)."""
+        tr.expand(p, x, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            tr.expand(p, x, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_us = e0.elapsed_time(e1) / reps * 1e3
+        amount = (T_loc + R) * H * b + 4 * T * K
+        ach = amount / t_us / 1e3
+        log(f"[bench] expand (alone)   {t_us:10.2f} us  {ach:9.1f} GB/s  "
+            f"{100 * ach / PEAK_HBM_GBS:5.1f}% of peak")
+        return {"us": t_us, "bound": "hbm", "achieved": ach, "unit": "GB/s", "peak": PEAK_HBM_GBS,
+                "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": amount, "launches": reps}
+
     if args.loop_only:
         print(json.dumps({"metric": METRIC, "value": tokens_per_s, "unit": "tokens/s",
-                          "ms_per_step": ms_step, "loop_only": True}), flush=True)
+                          "ms_per_step": ms_step, "loop_only": True,
+                          "expand_alone": expand_alone(args.steps)}), flush=True)
         return
     eager = {"ms_per_step": ms_step, "tokens_per_s": tokens_per_s,
              "launch": "plan + the stage entry points from Python, events between stages"}
@@ -414,8 +437,6 @@ def main():
     # mean device time of each stage over the timed steps, us per launch
     us = {name: sum(evs[i].elapsed_time(evs[i + 1]) for evs in step_events) / args.steps * 1e3
           for i, name in enumerate(stage_names)}
-    b = 2 if bf16 else 4
-    H, I, T, K = wl.H, wl.I, wl.T, wl.K
     peak_mm = PEAK_BF16_TFLOPS if bf16 else PEAK_F32_TFLOPS
     work = {
         # algorithmic bytes / flops per launch
@@ -462,6 +483,8 @@ def main():
         "launch": "one step captured in a HIP graph, replayed; stage times from the eager steps",
         "eager": eager,
     }
+    if gather:
+        result["expand_alone"] = expand_alone()
 
     if not args.no_lowbatch:
         result["lowbatch_combine"] = lowbatch_combine(args.steps)

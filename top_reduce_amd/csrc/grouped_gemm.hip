@@ -95,8 +95,18 @@ __device__ __forceinline__ int find_expert(const int* pre, int E, int v) {
   return lo;
 }
 
+// silu(g) * u = g u / (1 + e^-g), with the hardware exponential and
+// reciprocal (about 1 ulp each, far below the bf16 rounding of the result).
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+}
+
+// Two floats rounded to bf16 (nearest even) by one hardware conversion; lo in
+// bits 0..15.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // --------------------------------------------------------------------------
@@ -241,59 +251,79 @@ __device__ __forceinline__ void write_b(const Geo& g, const u32x4& v, int j) {
   stage_b<S>()[g.r_dst + j * 8 * kCpr] = v;
 }
 
-// The 16 MFMAs of register set P with the refill of stage S between them:
-// first the 8 activation DMAs of k-tile `dkt` of `ds`, then the 8 weight
-// pieces of k-tile kt + 2 from `r` into the stage, each followed by the
-// reload of its register with k-tile `lkt` of `ls`. Spreading the issues
-// keeps the MFMA pipe fed; the compiler's per-register waits gate each LDS
-// write on its own load only.
+// The 16 MFMAs of register set P with the 8 activation DMAs of k-tile `dkt`
+// of `ds` into stage S between them.
 template <int P, int S, bool G>
-__device__ __forceinline__ void mma_io(Frags& f, Regs& r, const Geo& g, const TileSrc<G>& ds,
-                                       int dkt, const TileSrc<G>& ls, int lkt) {
+__device__ __forceinline__ void mma_dma(Frags& f, const Geo& g, const TileSrc<G>& ds, int dkt) {
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
     const int i = m >> 2, j = m & 3;
     f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fb[P][j], f.fa[P][i], f.acc[i][j], 0, 0, 0);
-    if (m < kPieces) {
-      dma_a<S>(g, ds, dkt, m);
-    } else {
-      write_b<S>(g, r.v[m - kPieces], m - kPieces);
-      r.v[m - kPieces] = load_b(ls, lkt, m - kPieces);
+    if ((m & 1) == 0) dma_a<S>(g, ds, dkt, m >> 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The 16 MFMAs of register set P with weight pieces [J0, J0 + N) (N <= 3)
+// spread between them: each piece held in `r` goes to stage T, then its
+// register is reloaded with the piece of k-tile `lkt` of `ls` (the compiler's
+// per-register waits gate each LDS write on its own load only).
+template <int P, int T, int J0, int N, bool G>
+__device__ __forceinline__ void mma_wl(Frags& f, Regs& r, const Geo& g, const TileSrc<G>& ls,
+                                       int lkt) {
+#pragma unroll
+  for (int m = 0; m < 16; ++m) {
+    const int i = m >> 2, j = m & 3;
+    f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fb[P][j], f.fa[P][i], f.acc[i][j], 0, 0, 0);
+    if (m % 5 == 1 && m / 5 < N) {
+      write_b<T>(g, r.v[J0 + m / 5], J0 + m / 5);
+      r.v[J0 + m / 5] = load_b(ls, lkt, J0 + m / 5);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// One k-tile held in stage S, its first k-step's fragments already in
-// register set 0, the next k-tile's activations in flight into the other
-// stage (its weights already there). Fragment reads run one MFMA k-step ahead
-// (the scheduling barriers keep the compiler from sinking each read next to
-// its use). Before the last k-step's MFMAs the wave waits for its activation
-// DMA of the next k-tile (the weight loads issued after it, and the previous
-// tile's kStores output stores if `after_stores`, may stay in flight), drains its LDS traffic, meets the other waves and reads the next
-// k-tile's first fragments; the last k-step's MFMAs carry stage S's refill.
+// Step kt of the ring: k-tile kt in stage S (S = kt % 2), its first k-step's
+// fragments already in register set 0; the activations of k-tile kt + 1 in
+// flight into stage 1 - S and its weights in `r`. Fragment reads run one
+// MFMA k-step ahead (the scheduling barriers keep the compiler from sinking
+// each read next to its use).
+//  - The first three k-steps' MFMAs carry the weights of k-tile kt + 1 from
+//    `r` into stage 1 - S (no wave reads it during this step) and the loads
+//    of k-tile kt + 3 (`lkt` of `ls`) into the freed registers.
+//  - Then the wave waits for its activation DMA of k-tile kt + 1 (the weight
+//    loads issued after it, and the previous tile's kStores output stores if
+//    `after_stores`, may stay in flight), drains its LDS traffic, meets the
+//    other waves and reads the next k-tile's first fragments.
+//  - The last k-step's MFMAs carry the activation DMA of k-tile kt + 2
+//    (`dkt` of `ds`) into stage S, which every wave has now finished reading.
+//
+// The CU's vector memory path moves about 64 bytes a clock, so a k-tile's
+// 64 KiB of operand traffic takes about as long as a k-step's MFMAs, and LDS
+// writes compete with the fragment reads: issued together in one k-step they
+// stall the MFMAs queued behind them; spread over the k-tile they overlap.
 template <int S, bool kSwiglu, int kStores, bool G>
 __device__ __forceinline__ void ring_step(Frags& f, const Geo& g, Regs& r, bool after_stores,
                                           const TileSrc<G>& ds, int dkt, const TileSrc<G>& ls,
                                           int lkt) {
   read_frags<S, 1, kSwiglu>(f, g, 1);
   __builtin_amdgcn_sched_barrier(0);
-  mma<0>(f);
+  mma_wl<0, 1 - S, 0, 3>(f, r, g, ls, lkt);
   __builtin_amdgcn_sched_barrier(0);
   read_frags<S, 0, kSwiglu>(f, g, 2);
   __builtin_amdgcn_sched_barrier(0);
-  mma<1>(f);
+  mma_wl<1, 1 - S, 3, 3>(f, r, g, ls, lkt);
   __builtin_amdgcn_sched_barrier(0);
   read_frags<S, 1, kSwiglu>(f, g, 3);
   __builtin_amdgcn_sched_barrier(0);
-  mma<0>(f);
+  mma_wl<0, 1 - S, 6, 2>(f, r, g, ls, lkt);
   __builtin_amdgcn_sched_barrier(0);
   if (after_stores) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPieces + kStores, true));
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPieces, true));
   lds_barrier();
   read_frags<1 - S, 0, kSwiglu>(f, g, 0);
   __builtin_amdgcn_sched_barrier(0);
-  mma_io<1, S>(f, r, g, ds, dkt, ls, lkt);
+  mma_dma<1, S>(f, g, ds, dkt);
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -451,9 +481,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
 
   Regs r0, r1;
   {
-    int k0, k1, k2, k3;
-    const TileSrc<kGather> q0 = pick(0, k0), q1 = pick(1, k1), q2 = pick(2, k2),
-                           q3 = pick(3, k3);
+    int k0, k1, k2;
+    const TileSrc<kGather> q0 = pick(0, k0), q1 = pick(1, k1), q2 = pick(2, k2);
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) dma_a<0>(g, q0, k0, j);
 #pragma unroll
@@ -468,15 +497,9 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
       r0.v[j] = load_b(q2, k2, j);
       __builtin_amdgcn_sched_barrier(0);   // write before reload
     }
-#pragma unroll
-    for (int j = 0; j < kPieces; ++j) {
-      write_b<1>(g, r1.v[j], j);
-      r1.v[j] = load_b(q3, k3, j);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // the activation DMAs of k-tiles 0 and 1 (the weight loads after them
-    // may stay in flight)
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPieces, true));
+    // stage 0 whole; r1 holds k-tile 1's weights (written to stage 1 in step
+    // 0), r0 k-tile 2's; k-tile 1's activations may stay in flight
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kPieces, true));
     lds_barrier();
   }
   Frags f;
@@ -500,10 +523,11 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
           f.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zf, zf, floatx16{}, 0, 0, 0);
     }
 
-    // Stages alternate with the k-tile's parity (nk is even). Step kt waits
-    // for the activations of k-tile kt + 1 (issued one step earlier; after the
-    // previous tile's output stores for kt == 0) and refills its stage with
-    // k-tile kt + 2, loading k-tile kt + 4 into the freed registers.
+    // Stages alternate with the k-tile's parity (nk is even). Step kt writes
+    // the weights of k-tile kt + 1 from one register set and reloads it with
+    // k-tile kt + 3, waits for the activations of k-tile kt + 1 (issued one
+    // step earlier; after the previous tile's output stores for kt == 0) and
+    // sends the activations of k-tile kt + 2 to its own stage.
     // (a do-while: nk >= 2, and no zero-trip path for the accumulators; not
     // peeled or unrolled, so there is one copy of the step code)
     bool after_stores = !first;
@@ -513,13 +537,13 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     do {
       int dk, lk;
       {
-        const TileSrc<kGather> d = pick(kt + 2, dk), l = pick(kt + 4, lk);
-        ring_step<0, kSwiglu, kStores>(f, g, r0, after_stores, d, dk, l, lk);
+        const TileSrc<kGather> d = pick(kt + 2, dk), l = pick(kt + 3, lk);
+        ring_step<0, kSwiglu, kStores>(f, g, r1, after_stores, d, dk, l, lk);
       }
       after_stores = false;
       {
-        const TileSrc<kGather> d = pick(kt + 3, dk), l = pick(kt + 5, lk);
-        ring_step<1, kSwiglu, kStores>(f, g, r1, false, d, dk, l, lk);
+        const TileSrc<kGather> d = pick(kt + 3, dk), l = pick(kt + 4, lk);
+        ring_step<1, kSwiglu, kStores>(f, g, r0, false, d, dk, l, lk);
       }
       kt += 2;
     } while (kt < nk);
@@ -567,7 +591,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
               x0 = xg[v0];
               x1 = xg[v1];
             }
-            d[qq][h2] = pack_bf16x2(x0, x1);
+            d[qq][h2] = pack_bf16x2_hw(x0, x1);
           }
         }
         const int colj = t.n0 + (kSwiglu ? wn * 64 : wn * 128) + j * 32;
