@@ -69,9 +69,15 @@ def parse():
 
 
 def kernel_source_hash(name: str) -> str:
+    """First 16 hex digits of the sha256 of a kernel source's code, with
+    comments removed and whitespace runs collapsed (comment edits keep it)."""
     path = os.path.join(ROOT, "top_reduce_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def stored_traffic(kernel: str, config: str, src: str):

@@ -21,6 +21,10 @@ pytestmark = pytest.mark.gpu
 gen.custom_spec("mid", T=1024, K=8, E=8, G=64, H=1024, I=512, zipf_s=1.0, seed=7)
 gen.custom_spec("mid_small_experts", T=512, K=4, E=32, G=128, H=512, I=256, zipf_s=0.6, seed=8)
 gen.custom_spec("mid_f32", T=300, K=4, E=6, G=12, H=264, I=72, dtype="f32", zipf_s=0.5, seed=9)
+# every row routes to all 8 experts: 8 segments of 2080 rows, 9 m-tiles each
+# (the last one 32 rows deep); 288 tiles per GEMM, more than one round of the
+# persistent grid on 256 compute units.
+gen.custom_spec("rounds", T=2080, K=8, E=8, G=8, H=1024, I=512, routing="uniform", seed=10)
 
 
 def _assert_close(got, ref, dtype, what):
@@ -38,7 +42,7 @@ def _forward(wl, flags=0, y_alias=False, weights=True):
     return p, host(y)
 
 
-@pytest.mark.parametrize("name,flags", [("c1", 0), ("mid_f32", 0), ("mid", 0),
+@pytest.mark.parametrize("name,flags", [("c1", 0), ("mid_f32", 0), ("mid", 0), ("rounds", 0),
                                         ("mid", tr.FLAG_GEMM_FORCE_TILED),
                                         ("mid", tr.FLAG_GEMM_FORCE_STREAM),
                                         ("mid_small_experts", 0)])
@@ -85,7 +89,7 @@ def test_forward_full_size_sampled(name):
     _assert_close(as_f64(y[toks]), ref, wl.dtype, f"{name} y[{len(toks)} rows]")
 
 
-@pytest.mark.parametrize("name", ["mid", "c1"])
+@pytest.mark.parametrize("name", ["mid", "c1", "rounds"])
 def test_stages(name):
     """expand bit-exact; O rows vs the oracle's per-route MLP; reduce."""
     say(f"stages {name}")
@@ -190,7 +194,8 @@ def test_error_convention_on_device():
 
 @pytest.mark.parametrize("name,flags", [("mid", 0), ("mid", tr.FLAG_GEMM_FORCE_TILED),
                                         ("mid", tr.FLAG_GEMM_FORCE_STREAM),
-                                        ("mid_small_experts", 0), ("mid_f32", 0), ("c1", 0)])
+                                        ("mid_small_experts", 0), ("mid_f32", 0), ("c1", 0),
+                                        ("rounds", 0)])
 def test_up_x_equals_expand_then_up(name, flags):
     """GEMM1 gathering the received rows through the route table computes the
     same h, bit for bit, as expand followed by GEMM1 over Xe: the same rows

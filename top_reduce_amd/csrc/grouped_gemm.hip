@@ -1,5 +1,6 @@
 // moe_grouped_gemm: the local experts' SwiGLU MLP over the expert-contiguous
-// rows Xe (DeepEP issue #48 answer: a grouped GEMM over expanded tokens).
+// rows Xe, or over x read through the route table (DeepEP issue #48 answer: a
+// grouped GEMM over expanded tokens).
 //
 //   GEMM1 + SwiGLU: h[r, i] = silu(Xe[r] . W1[e][i]) * (Xe[r] . W1[e][I + i])
 //   GEMM2:          O[r, j] = h[r] . W2[e][j]
@@ -17,11 +18,13 @@
 //    (v_mfma_f32_32x32x16_bf16), four waves each owning a 128x128 quadrant,
 //    operands staged through two XOR-swizzled LDS stages: activation rows by
 //    buffer->LDS DMA one k-tile ahead, weight rows through registers loaded
-//    four k-tiles ahead. Tiles are numbered expert-major with groups of 4 m-tiles and
-//    handed to the 8 XCDs in contiguous chunks so that concurrent tiles of an
-//    XCD share A and B tiles in its L2. For GEMM1 each B tile holds 128 gate
-//    rows and the matching 128 up rows, so a lane owns gate and up of the
-//    same outputs and SwiGLU runs in the epilogue.
+//    two k-tiles ahead and written to LDS one k-tile ahead, both spread over
+//    the k-steps' MFMAs. With GEMM1 gathering, the activation rows come
+//    straight from x through the route table. Tiles are numbered expert-major
+//    with groups of 4 m-tiles and handed to the 8 XCDs in contiguous chunks so
+//    that concurrent tiles of an XCD share A and B tiles in its L2. For GEMM1
+//    each B tile holds 128 gate rows and the matching 128 up rows, so a lane
+//    owns gate and up of the same outputs and SwiGLU runs in the epilogue.
 //  - gemm_stream: experts with few rows (decode). Weight rows are streamed
 //    once from HBM straight into the A operand of v_mfma_f32_16x16x32_bf16;
 //    up to 32 token rows ride in the B operand; the reduction dimension is
