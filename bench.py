@@ -3,8 +3,9 @@
 
 One step = the whole hot path on one batch: moe_plan (route scan), then the
 kernels moe_forward runs (for bf16: grouped SwiGLU GEMM up gathering the
-received rows, GEMM down, weighted top-k reduce; for fp32 an expand pass
-first) through their stage entry points, on synthetic inputs already resident
+received rows, GEMM down writing the rows of received rows with one local
+slot straight to the output, the weighted top-k reduce of the others; for
+fp32: expand, GEMM up, GEMM down, reduce) through their stage entry points, on synthetic inputs already resident
 in HBM. Default workload: the prefill shape
 (16384 received tokens, H=7168, I=2048, 32 local experts of 256, top-8, Zipf
 s=1.0 popularity), bf16.
@@ -312,7 +313,10 @@ def main():
     p = step()
     R, T_loc, _, n_empty = tr.plan_stats(p)
     real_rows = int(wl.real.sum())
-    log(f"[bench] R={R} T_loc={T_loc} real_rows={real_rows} empty_experts={n_empty}")
+    # received rows with exactly one local slot (GEMM2 writes them to y)
+    n_single = int((p.views()["row_dst"][:R] >= 0).sum()) if R else 0
+    log(f"[bench] R={R} T_loc={T_loc} real_rows={real_rows} empty_experts={n_empty} "
+        f"single_slot_rows={n_single}")
 
     if args.copy_calibration_mib:
         # A plain elementwise kernel over a known number of bytes: its HBM
@@ -327,11 +331,11 @@ def main():
         del src, dst
 
     # One step = plan (route scan) + forward: the same kernels moe_forward
-    # launches (bf16: GEMM up gathering x through the route table, GEMM down,
-    # combine-reduce; fp32: expand, GEMM up over the expanded rows, GEMM down,
-    # combine-reduce), called stage by stage so that events between the
-    # stages, on the launch stream, give each kernel's device time inside the
-    # timed region.
+    # launches (bf16: GEMM up gathering x through the route table, GEMM down
+    # writing single-slot rows to y, the reduce of the other rows; fp32:
+    # expand, GEMM up over the expanded rows, GEMM down, reduce), called
+    # stage by stage so that events between the stages, on the launch stream,
+    # give each kernel's device time inside the timed region.
     gather = bf16 and wl.T * wl.H * 2 <= 0x7FFFFFFF
     stage_names = (("route_scan", "gemm_up", "gemm_down", "combine_reduce") if gather else
                    ("route_scan", "expand", "gemm_up", "gemm_down", "combine_reduce"))
@@ -351,10 +355,16 @@ def main():
             tr.grouped_gemm_up(q, w1, stream=stream)
         i += 1
         evs[i].record(stream)
-        tr.grouped_gemm_down(q, w2, stream=stream)
+        if gather:
+            tr.grouped_gemm_down_y(q, w2, w, y, stream=stream)
+        else:
+            tr.grouped_gemm_down(q, w2, stream=stream)
         i += 1
         evs[i].record(stream)
-        tr.combine_reduce(q, w, y=y, stream=stream)
+        if gather:
+            tr.combine_reduce_multi(q, w, y, stream=stream)
+        else:
+            tr.combine_reduce(q, w, y=y, stream=stream)
         evs[i + 1].record(stream)
 
     def new_events():
@@ -453,6 +463,9 @@ def main():
     }
     if gather:
         del work["expand"]
+        # the reduce reads the rows of received rows with several local slots
+        # and writes those and the rows without a local slot
+        work["combine_reduce"] = ("hbm", (R - n_single) * H * b + (T - n_single) * H * b + 8 * T * K)
     stages = {"route_scan": {"us": us["route_scan"]}}
     for k, (bound, amount) in work.items():
         t_s = us[k] / 1e6
@@ -482,7 +495,8 @@ def main():
         "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
         "config": {"workload": f"{args.config} {WORKLOAD_NAMES[args.config]}", "T": T,
                    "real_rows": real_rows, "K": K, "E_local": wl.E, "E_global": wl.G, "H": H,
-                   "I": I, "R": R, "T_loc": T_loc, "empty_experts": n_empty, "seed": wl.seed,
+                   "I": I, "R": R, "T_loc": T_loc, "single_slot_rows": n_single,
+                   "empty_experts": n_empty, "seed": wl.seed,
                    "parallelism": "single GPU"},
         "roofline": roofline,
         "stages": stages,

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TR_ABI_VERSION 2
+#define TR_ABI_VERSION 3
 
 typedef enum {
     TR_OK = 0,
@@ -95,13 +95,20 @@ typedef struct tr_moe_plan {
     int32_t* row_map;      /* [T*K] expanded row of slot (t,k), or -1 */
     int32_t* row_src;      /* [R_cap] received row of expanded row r (r < R) */
     int32_t* row_k;        /* [R_cap] slot of expanded row r (r < R) */
-    int32_t* stats;        /* [4] R, rows with >= 1 local route, ignored slots, empty experts */
+    int32_t* stats;        /* [5] R, rows with >= 1 local route, ignored slots, empty
+                              experts, entries of tok_rest */
     int32_t* scan_tmp;     /* route-scan block partials */
     void* Xe;              /* [R_cap + 256, H] expanded rows (expert-contiguous) */
     void* h;               /* [R_cap + 256, I] silu(gate) * up */
     void* O;               /* [R_cap, H] expert outputs */
     int32_t scan_blocks;
     int32_t scan_rows_per_block;
+    int32_t* row_dst;      /* [R_cap] for expanded row r < R: slot t*K + k if its
+                              received row t has exactly one local slot and its
+                              expert is one the tiled GEMM takes (see
+                              moe_grouped_gemm_down_y), else -1 */
+    int32_t* tok_rest;     /* [T] the other received rows, in no particular order;
+                              stats[4] of them */
 } tr_moe_plan;
 
 /* Bytes of device workspace a plan for `desc` needs (every buffer above,
@@ -126,9 +133,12 @@ tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size
  * w1: device [E, 2I, H] (rows [0, I) gate, [I, 2I) up); w2: device [E, H, I];
  * y: device [T, H], may alias x; no other aliasing. Accumulation is fp32;
  * for bf16 the intermediate h and expert outputs are rounded to bf16.
- * Equivalent to moe_expand, moe_grouped_gemm, moe_combine_reduce(plan, NULL,
- * topk_weights, y); for bf16 it runs moe_grouped_gemm_up_x,
- * moe_grouped_gemm_down and moe_combine_reduce, so Xe is not written. */
+ * y equals, bit for bit, moe_expand, moe_grouped_gemm and
+ * moe_combine_reduce(plan, NULL, topk_weights, y). For bf16 with
+ * T * H * 2 < 2^31 it runs moe_grouped_gemm_up_x, moe_grouped_gemm_down_y and
+ * moe_combine_reduce_multi instead (the fused forms of expand and of the
+ * reduce): Xe is not written, and O only for received rows with several
+ * local slots. */
 tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_weights,
                       const void* w1, const void* w2, void* y, hipStream_t stream);
 
@@ -155,6 +165,18 @@ tr_status moe_grouped_gemm_up(const tr_moe_plan* plan, const void* w1, hipStream
 tr_status moe_grouped_gemm_up_x(const tr_moe_plan* plan, const void* x, const void* w1,
                                 hipStream_t stream);
 tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStream_t stream);
+/* GEMM2 with the weighted reduce folded into its epilogue for received rows
+ * with exactly one local slot whose expert the tiled kernel takes (more than
+ * 32 routes; every expert with TR_FLAG_GEMM_FORCE_TILED, none with
+ * TR_FLAG_GEMM_FORCE_STREAM): the plan's row_dst. Such a row's output is
+ * rounded to bf16 as O would be, weighted and rounded again exactly as
+ * moe_combine_reduce does, and written straight to y[t]; the other rows go to
+ * O. topk_weights: device fp32 [T, K] or NULL (weight 1); y: device [T, H],
+ * must not overlap h or O. moe_combine_reduce_multi then completes y. bf16 with
+ * T * H * 2 < 2^31 only; otherwise TR_EUNSUPPORTED (use moe_grouped_gemm_down
+ * and moe_combine_reduce). */
+tr_status moe_grouped_gemm_down_y(const tr_moe_plan* plan, const void* w2,
+                                  const float* topk_weights, void* y, hipStream_t stream);
 
 /* Weighted top-k reduce (DeepEP issue #48: the reduction before the combine
  * all-to-all; DeepEP issue #760: the combine epilogue, one row per received
@@ -166,6 +188,11 @@ tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStre
  * occupy many compute units. */
 tr_status moe_combine_reduce(const tr_moe_plan* plan, const void* expert_out,
                              const float* topk_weights, void* y, hipStream_t stream);
+
+/* moe_combine_reduce over the plan's O for the received rows in the plan's
+ * tok_rest only; the others are left as moe_grouped_gemm_down_y wrote them. */
+tr_status moe_combine_reduce_multi(const tr_moe_plan* plan, const float* topk_weights, void* y,
+                                   hipStream_t stream);
 
 /* Cross-rank combine epilogue (DeepEP issue #760, body: after combine's
  * all-to-all, every output token sums the rows returned by the ranks that

@@ -26,7 +26,8 @@ def test_header_declares_entry_points():
     names = _declared()
     for n in ("moe_workspace_size", "moe_plan", "moe_forward", "moe_expand", "moe_grouped_gemm",
               "moe_combine_reduce", "moe_plan_stats", "moe_grouped_gemm_up", "moe_grouped_gemm_down",
-              "moe_combine_epilogue", "moe_grouped_gemm_up_x", "moe_last_error",
+              "moe_combine_epilogue", "moe_grouped_gemm_up_x", "moe_grouped_gemm_down_y",
+              "moe_combine_reduce_multi", "moe_last_error",
               "moe_abi_version"):
         assert n in names
 
@@ -113,11 +114,26 @@ def test_entry_points_reject_null_plan():
     assert lib.moe_grouped_gemm_up(None, None, None) == -1
     assert lib.moe_grouped_gemm_up_x(None, None, None, None) == -1
     assert lib.moe_grouped_gemm_down(None, None, None) == -1
+    assert lib.moe_grouped_gemm_down_y(None, None, None, None, None) == -1
+    assert lib.moe_combine_reduce_multi(None, None, None, None) == -1
     assert lib.moe_combine_reduce(None, None, None, None, None) == -1
     assert lib.moe_plan_stats(None, None, None) == -1
     empty = B.PlanStruct()            # no workspace
     assert lib.moe_forward(C.byref(empty), None, None, None, None, None, None) == -1
     assert b"workspace" in lib.moe_last_error()
+
+
+def test_fused_down_is_bf16_only_and_checked_on_the_host():
+    lib = tr.load_library()
+    st = B.PlanStruct()
+    st.d = tr.make_desc(T=8, K=2, E=4, H=104, I=72, dtype=torch.float32)
+    fake = C.c_void_p(1 << 40)           # never dereferenced: checks fail first
+    st.ws = fake
+    assert lib.moe_grouped_gemm_down_y(C.byref(st), fake, None, fake, None) == -2
+    assert b"bf16" in lib.moe_last_error()
+    st.d = tr.make_desc(T=8, K=2, E=4, H=512, I=128)
+    assert lib.moe_grouped_gemm_down_y(C.byref(st), fake, None, None, None) == -1
+    assert b"y" in lib.moe_last_error()
 
 
 def test_forward_rejects_misaligned_buffers():

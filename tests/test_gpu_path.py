@@ -234,3 +234,31 @@ def test_up_x_decode(T):
     tr.grouped_gemm_up_x(p, d["x"], d["w1"])
     torch.cuda.synchronize()
     assert np.array_equal(host(v["h"][:R]).view(np.uint8), h_ref.view(np.uint8))
+
+
+@pytest.mark.parametrize("name,flags,T", [("mid", 0, None), ("mid", tr.FLAG_GEMM_FORCE_TILED, None),
+                                          ("mid", tr.FLAG_GEMM_FORCE_STREAM, None),
+                                          ("mid_small_experts", 0, None), ("rounds", 0, None),
+                                          ("c3", 0, 1), ("c3", 0, 64), ("c4", 0, None),
+                                          ("c2", 0, None), ("c5", 0, None)])
+def test_forward_fused_equals_stages(name, flags, T):
+    """moe_forward (GEMM1 gathering x, GEMM2 writing rows of received rows
+    with one local slot straight to y, the reduce for the rest) equals the
+    unfused composition expand -> grouped GEMM -> reduce bit for bit, with
+    and without weights; so do the fused stage entry points."""
+    say(f"fused forward {name} flags={flags} T={T}")
+    wl = gen.make_workload(name, T=T, variant="random" if name == "c3" else "", with_weights=True)
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch_dtype(wl), flags=flags)
+    for w in (d["w"], None):
+        y_f = tr.forward(p, d["x"], w, d["w1"], d["w2"])
+        tr.expand(p, d["x"])
+        tr.grouped_gemm(p, d["w1"], d["w2"])
+        y_s = tr.combine_reduce(p, w)
+        y_3 = torch.full_like(y_s, float("nan"))
+        tr.grouped_gemm_up_x(p, d["x"], d["w1"])
+        tr.grouped_gemm_down_y(p, d["w2"], w, y_3)
+        tr.combine_reduce_multi(p, w, y_3)
+        torch.cuda.synchronize()
+        assert torch.equal(y_f.view(torch.int16), y_s.view(torch.int16)), "forward != stages"
+        assert torch.equal(y_3.view(torch.int16), y_s.view(torch.int16)), "fused stages != stages"

@@ -1,5 +1,5 @@
 """moe_route_scan on the GPU vs the oracle: bit-exact counts, offsets,
-row_map, row_src, row_k and stats, for every workload at full size and for
+row_map, row_src, row_k, row_dst and stats, for every workload at full size and for
 edge cases (empty, all padding, one hot expert, duplicates, foreign ids,
 int32 ids, expert_begin, maximal E, ragged multi-block inputs)."""
 
@@ -29,6 +29,22 @@ def _check(idx_np, E, eb=0, idx_dtype=torch.int64, H=256, I=128):
     assert np.array_equal(v["row_map"].cpu().numpy(), ref["row_map"])
     assert np.array_equal(v["row_src"][:R].cpu().numpy(), ref["row_src"])
     assert np.array_equal(v["row_k"][:R].cpu().numpy(), ref["row_k"])
+    # row_dst by its definition from the oracle's route: the slot of a
+    # received row with exactly one local slot whose expert has more than 32
+    # routes (the tiled GEMM's experts), -1 for every other row
+    rm = ref["row_map"]
+    n_loc = (rm >= 0).sum(1)
+    want = np.full(R, -1, np.int64)
+    tt, kk = np.nonzero((rm >= 0) & (n_loc[:, None] == 1))
+    tiled = ref["counts"][idx_np[tt, kk] - eb] > 32
+    tt, kk = tt[tiled], kk[tiled]
+    want[rm[tt, kk]] = tt * K + kk
+    assert np.array_equal(v["row_dst"][:R].cpu().numpy(), want)
+    # tok_rest: every other received row, in any order
+    rest = np.setdiff1d(np.arange(T), tt)
+    n_rest = int(v["stats"][4])
+    assert n_rest == rest.size
+    assert np.array_equal(np.sort(v["tok_rest"][:n_rest].cpu().numpy()), rest)
     local = (idx_np >= eb) & (idx_np < eb + E)
     assert stats == (R, int(local.any(1).sum()) if T else 0, int((~local).sum()),
                      int((ref["counts"] == 0).sum()))

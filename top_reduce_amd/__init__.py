@@ -19,10 +19,12 @@ from ._binding import (  # noqa: F401
     TopReduceError,
     combine_epilogue,
     combine_reduce,
+    combine_reduce_multi,
     expand,
     forward,
     grouped_gemm,
     grouped_gemm_down,
+    grouped_gemm_down_y,
     grouped_gemm_up,
     grouped_gemm_up_x,
     lib_path,

@@ -17,7 +17,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libtopreduce.so"
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 BF16, F32 = 0, 1
 IDX_I32, IDX_I64 = 0, 1
 FLAG_GEMM_FORCE_TILED = 0x1
@@ -45,7 +45,8 @@ class PlanStruct(C.Structure):
                 ("row_src", C.c_void_p), ("row_k", C.c_void_p), ("stats", C.c_void_p),
                 ("scan_tmp", C.c_void_p), ("Xe", C.c_void_p), ("h", C.c_void_p),
                 ("O", C.c_void_p), ("scan_blocks", C.c_int32),
-                ("scan_rows_per_block", C.c_int32)]
+                ("scan_rows_per_block", C.c_int32), ("row_dst", C.c_void_p),
+                ("tok_rest", C.c_void_p)]
 
 
 _lib = None
@@ -82,6 +83,10 @@ def load_library():
     lib.moe_grouped_gemm_down.argtypes = [C.POINTER(PlanStruct), vp, vp]
     lib.moe_combine_reduce.restype = st
     lib.moe_combine_reduce.argtypes = [C.POINTER(PlanStruct), vp, vp, vp, vp]
+    lib.moe_grouped_gemm_down_y.restype = st
+    lib.moe_grouped_gemm_down_y.argtypes = [C.POINTER(PlanStruct), vp, vp, vp, vp]
+    lib.moe_combine_reduce_multi.restype = st
+    lib.moe_combine_reduce_multi.argtypes = [C.POINTER(PlanStruct), vp, vp, vp]
     lib.moe_grouped_gemm_up_x.restype = st
     lib.moe_grouped_gemm_up_x.argtypes = [C.POINTER(PlanStruct), vp, vp, vp]
     lib.moe_combine_epilogue.restype = st
@@ -184,7 +189,9 @@ class MoePlan:
             row_map=self._view(s.row_map, d.T * d.K, torch.int32, (d.T, d.K)),
             row_src=self._view(s.row_src, s.R_cap, torch.int32, (s.R_cap,)),
             row_k=self._view(s.row_k, s.R_cap, torch.int32, (s.R_cap,)),
-            stats=self._view(s.stats, 4, torch.int32, (4,)),
+            row_dst=self._view(s.row_dst, s.R_cap, torch.int32, (s.R_cap,)),
+            tok_rest=self._view(s.tok_rest, d.T, torch.int32, (d.T,)),
+            stats=self._view(s.stats, 5, torch.int32, (5,)),
             Xe=self._view(s.Xe, s.R_cap * d.H, dt, (s.R_cap, d.H)),
             h=self._view(s.h, s.R_cap * d.I, dt, (s.R_cap, d.I)),
             O=self._view(s.O, s.R_cap * d.H, dt, (s.R_cap, d.H)),
@@ -280,6 +287,33 @@ def grouped_gemm_down(p: MoePlan, w2: torch.Tensor, stream=None) -> None:
     w2p = _dev_tensor(w2, "w2", _torch_dtype(d.dtype), (d.E, d.H, d.I))
     _check(load_library().moe_grouped_gemm_down(C.byref(p.struct), C.c_void_p(w2p or None),
                                                 _stream_ptr(stream, p.ws.device)))
+
+
+def grouped_gemm_down_y(p: MoePlan, w2: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                        y: torch.Tensor, stream=None) -> None:
+    """moe_grouped_gemm_down_y: GEMM2 writing rows of received rows with one
+    local slot straight to y (weighted), the others to O."""
+    d = p.desc
+    dt = _torch_dtype(d.dtype)
+    w2p = _dev_tensor(w2, "w2", dt, (d.E, d.H, d.I))
+    yp = _dev_tensor(y, "y", dt, (d.T, d.H))
+    wp = _opt_weights(p, topk_weights)
+    _check(load_library().moe_grouped_gemm_down_y(C.byref(p.struct), C.c_void_p(w2p or None),
+                                                  C.c_void_p(wp), C.c_void_p(yp or None),
+                                                  _stream_ptr(stream, p.ws.device)))
+
+
+def combine_reduce_multi(p: MoePlan, topk_weights: Optional[torch.Tensor], y: torch.Tensor,
+                         stream=None) -> torch.Tensor:
+    """moe_combine_reduce_multi: the reduce for received rows with zero or
+    several local slots (after grouped_gemm_down_y)."""
+    d = p.desc
+    yp = _dev_tensor(y, "y", _torch_dtype(d.dtype), (d.T, d.H))
+    wp = _opt_weights(p, topk_weights)
+    _check(load_library().moe_combine_reduce_multi(C.byref(p.struct), C.c_void_p(wp),
+                                                   C.c_void_p(yp or None),
+                                                   _stream_ptr(stream, p.ws.device)))
+    return y
 
 
 def combine_reduce(p: MoePlan, topk_weights: Optional[torch.Tensor],

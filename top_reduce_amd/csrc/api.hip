@@ -62,7 +62,8 @@ tr_status check_desc(const tr_moe_desc* d) {
 struct Layout {
   int64_t R_cap;
   int blocks, rpb;
-  size_t stats, counts, offsets, row_map, row_src, row_k, scan_tmp, Xe, h, O, total;
+  size_t stats, counts, offsets, row_map, row_src, row_k, row_dst, tok_rest, scan_tmp, Xe, h, O,
+      total;
 };
 
 Layout layout(const tr_moe_desc& d) {
@@ -79,6 +80,8 @@ Layout layout(const tr_moe_desc& d) {
   L.row_map = take(sizeof(int32_t) * d.T * d.K);
   L.row_src = take(sizeof(int32_t) * L.R_cap);
   L.row_k = take(sizeof(int32_t) * L.R_cap);
+  L.row_dst = take(sizeof(int32_t) * L.R_cap);
+  L.tok_rest = take(sizeof(int32_t) * d.T);
   L.scan_tmp = take(sizeof(int32_t) * static_cast<size_t>(L.blocks) * (d.E + 2));
   L.Xe = take(es * (L.R_cap + tr::kRowPad) * d.H);
   L.h = take(es * (L.R_cap + tr::kRowPad) * d.I);
@@ -153,6 +156,8 @@ tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size
   p.row_map = reinterpret_cast<int32_t*>(b + L.row_map);
   p.row_src = reinterpret_cast<int32_t*>(b + L.row_src);
   p.row_k = reinterpret_cast<int32_t*>(b + L.row_k);
+  p.row_dst = reinterpret_cast<int32_t*>(b + L.row_dst);
+  p.tok_rest = reinterpret_cast<int32_t*>(b + L.tok_rest);
   p.scan_tmp = reinterpret_cast<int32_t*>(b + L.scan_tmp);
   p.Xe = b + L.Xe;
   p.h = b + L.h;
@@ -233,6 +238,34 @@ tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStre
                     "moe_grouped_gemm_down launch");
 }
 
+tr_status moe_grouped_gemm_down_y(const tr_moe_plan* plan, const void* w2,
+                                  const float* topk_weights, void* y, hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  const bool any = plan->d.T > 0;
+  if ((s = check_buf(w2, "w2", any)) != TR_OK) return s;
+  if ((s = check_buf(y, "y", any)) != TR_OK) return s;
+  if (topk_weights && !aligned(topk_weights, 4)) return fail(TR_EINVAL, "topk_weights misaligned");
+  if (!tr::gemm_can_gather(plan->d))
+    return fail(TR_EUNSUPPORTED, "moe_grouped_gemm_down_y needs bf16 and T * H * 2 < 2^31");
+  if (!any) return ok();
+  return hip_status(tr::grouped_gemm(*plan, nullptr, w2, tr::kGemmDown, stream, nullptr,
+                                     topk_weights, y),
+                    "moe_grouped_gemm_down_y launch");
+}
+
+tr_status moe_combine_reduce_multi(const tr_moe_plan* plan, const float* topk_weights, void* y,
+                                   hipStream_t stream) {
+  tr_status s = check_plan(plan);
+  if (s != TR_OK) return s;
+  const bool any = plan->d.T > 0;
+  if ((s = check_buf(y, "y", any)) != TR_OK) return s;
+  if (topk_weights && !aligned(topk_weights, 4)) return fail(TR_EINVAL, "topk_weights misaligned");
+  if (!any) return ok();
+  return hip_status(tr::combine_reduce(*plan, nullptr, topk_weights, y, stream, true),
+                    "moe_combine_reduce_multi launch");
+}
+
 tr_status moe_combine_reduce(const tr_moe_plan* plan, const void* expert_out,
                              const float* topk_weights, void* y, hipStream_t stream) {
   tr_status s = check_plan(plan);
@@ -258,10 +291,15 @@ tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_
   if (topk_weights && !aligned(topk_weights, 4)) return fail(TR_EINVAL, "topk_weights misaligned");
   if (!any) return ok();
   if (tr::gemm_can_gather(plan->d)) {
-    // GEMM1 reads x through the route table: no expand pass, Xe unused
-    if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream, x),
+    // GEMM1 reads x through the route table (no expand pass, Xe unused);
+    // GEMM2 writes received rows with one local slot straight to y, and the
+    // reduce completes the others
+    if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream, x,
+                                         topk_weights, y),
                         "moe_grouped_gemm launch")) != TR_OK)
       return s;
+    return hip_status(tr::combine_reduce(*plan, nullptr, topk_weights, y, stream, true),
+                      "moe_combine_reduce launch");
   } else {
     if ((s = hip_status(tr::expand(*plan, x, stream), "moe_expand launch")) != TR_OK) return s;
     if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream),

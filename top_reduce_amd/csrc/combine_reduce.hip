@@ -67,21 +67,23 @@ struct Row8<false> {
   }
 };
 
-// Rows at or past n_rows count as absent, like -1.
+// Rows at or past n_rows count as absent, like -1. With `rest`, only the
+// tokens rest[0 .. *rest_n) are written (the others have exactly one local
+// slot, and GEMM2 has written them).
 template <bool kBF16>
 __global__ __launch_bounds__(kThreads) void combine_rows(const void* __restrict__ O,
                                                          const int* __restrict__ row_map,
                                                          const float* __restrict__ w, int64_t T,
                                                          int K, int64_t H, int64_t n_rows,
+                                                         const int* __restrict__ rest,
+                                                         const int* __restrict__ rest_n,
                                                          void* __restrict__ y) {
   const int64_t nslab = (H + kSlab - 1) / kSlab;
-  const int64_t items = T * nslab;
   const int lane = lane_id();
   const int64_t gw = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) / kWave;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  for (int64_t item = gw; item < items; item += nw) {
-    const int64_t t = __builtin_amdgcn_readfirstlane(static_cast<int>(item / nslab));
-    const int64_t col = (item - t * nslab) * kSlab + static_cast<int64_t>(lane) * 8;
+  // y[t] over the slab of columns starting at col (this lane: col .. col + 7)
+  auto reduce_slab = [&](int64_t t, int64_t col) {
     const bool active = col < H;
     float acc[8];
 #pragma unroll
@@ -110,6 +112,13 @@ __global__ __launch_bounds__(kThreads) void combine_rows(const void* __restrict_
         }
     }
     if (active) Row8<kBF16>::store(y, t * H + col, acc);
+  };
+  const int64_t ntok = rest ? *rest_n : T;
+  const int64_t items = ntok * nslab;
+  for (int64_t item = gw; item < items; item += nw) {
+    const int64_t q = __builtin_amdgcn_readfirstlane(static_cast<int>(item / nslab));
+    const int64_t t = rest ? rest[q] : q;
+    reduce_slab(t, (item - q * nslab) * kSlab + static_cast<int64_t>(lane) * 8);
   }
 }
 
@@ -118,7 +127,8 @@ __global__ __launch_bounds__(kThreads) void combine_rows(const void* __restrict_
 namespace {
 
 hipError_t launch_rows(bool bf16, const void* O, const int* row_map, const float* w, int64_t T,
-                       int K, int64_t H, int64_t n_rows, void* y, hipStream_t st) {
+                       int K, int64_t H, int64_t n_rows, const int* rest, const int* rest_n,
+                       void* y, hipStream_t st) {
   const int64_t nslab = (H + kSlab - 1) / kSlab;
   const int64_t waves = T * nslab;
   int64_t blocks = cdiv(waves, kThreads / kWave);
@@ -127,20 +137,22 @@ hipError_t launch_rows(bool bf16, const void* O, const int* row_map, const float
   if (blocks < 1) return hipSuccess;
   if (bf16)
     hipLaunchKernelGGL(combine_rows<true>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       st, O, row_map, w, T, K, H, n_rows, y);
+                       st, O, row_map, w, T, K, H, n_rows, rest, rest_n, y);
   else
     hipLaunchKernelGGL(combine_rows<false>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
-                       st, O, row_map, w, T, K, H, n_rows, y);
+                       st, O, row_map, w, T, K, H, n_rows, rest, rest_n, y);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const float* w, void* y,
-                          hipStream_t st) {
+                          hipStream_t st, bool skip_single) {
   const tr_moe_desc& d = p.d;
   const void* O = expert_out ? expert_out : p.O;
-  return launch_rows(d.dtype == TR_BF16, O, p.row_map, w, d.T, d.K, d.H, p.R_cap, y, st);
+  return launch_rows(d.dtype == TR_BF16, O, p.row_map, w, d.T, d.K, d.H, p.R_cap,
+                     skip_single ? p.tok_rest : nullptr, skip_single ? p.stats + 4 : nullptr, y,
+                     st);
 }
 
 // The cross-rank epilogue is the same reduction with unit weights over the
@@ -149,7 +161,7 @@ hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const fl
 // the first proposed fix).
 hipError_t combine_epilogue(int64_t T, int J, int64_t H, bool bf16, const int* src,
                             const void* recv, int64_t n_recv, void* y, hipStream_t st) {
-  return launch_rows(bf16, recv, src, nullptr, T, J, H, n_recv, y, st);
+  return launch_rows(bf16, recv, src, nullptr, T, J, H, n_recv, nullptr, nullptr, y, st);
 }
 
 }  // namespace tr

@@ -58,6 +58,14 @@ struct GemmArgs {
   int64_t a_rows;       // rows allocated in A: R_cap + BM (gather: the rows of x)
   const int* gather;    // GEMM1 straight from the received rows: A row r of the
                         // expanded order is row gather[r] of A (x); NULL: A is Xe
+  // GEMM2 with the reduce folded in for received rows with one local slot
+  // (rows of tiled experts only): row r goes to y[dst[r] / K] weighted by
+  // wts[dst[r]] (dst[r] >= 0), not O
+  const int* dst;       // the plan's row_dst, or NULL: every row goes to O
+  const float* wts;     // [T, K] gate weights, or NULL for weight 1
+  void* y;              // [T, Nc]
+  int K;
+  int64_t T;
 };
 
 // Builds in LDS the exclusive prefix of `units(e)` over experts; returns the
@@ -533,6 +541,18 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     // sends the activations of k-tile kt + 2 to its own stage.
     // (a do-while: nk >= 2, and no zero-trip path for the accumulators; not
     // peeled or unrolled, so there is one copy of the step code)
+    // reduce folded into GEMM2: the slots of this lane's four rows, loaded
+    // here so that they have arrived by the epilogue
+    const bool fused = !kSwiglu && a.dst != nullptr;
+    int slot[4];
+    if (fused) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + (lane & 31);
+        slot[i] = row < t.rows_valid ? a.dst[t.row0 + row] : -1;
+      }
+    }
+
     bool after_stores = !first;
     first = false;
     int kt = 0;
@@ -564,6 +584,17 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
         Cb + static_cast<int64_t>(t.row0) * a.Nc, 0, static_cast<int>(out_left), kBufferFlags);
     const int hi = lane >> 5;
+    // reduce folded into GEMM2: each lane's four rows' y row and weight
+    int yrow[4];
+    float ywt[4];
+    uint16_t* __restrict__ Yb = static_cast<uint16_t*>(a.y);
+    if (fused) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        yrow[i] = slot[i] >= 0 ? slot[i] / a.K : -1;
+        ywt[i] = (slot[i] >= 0 && a.wts) ? a.wts[slot[i]] : 1.0f;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t row_off = static_cast<uint32_t>(wm * 128 + i * 32 + (lane & 31)) * a.Nc;
@@ -605,7 +636,28 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
           const auto s1 = __builtin_amdgcn_permlane32_swap(d[qq][1], d[qq + 1][1], false, false);
           const u32x4 out = u32x4{s0[0], s1[0], s0[1], s1[1]};
           const uint32_t col = colj + 8 * (qq + hi);
-          __builtin_amdgcn_raw_buffer_store_b128(out, rC, (row_off + col) * 2, 0, 0);
+          if (!fused) {
+            __builtin_amdgcn_raw_buffer_store_b128(out, rC, (row_off + col) * 2, 0, 0);
+          } else {
+            // a row of a received row with one local slot goes to y exactly
+            // as the reduce writes it: fma(w, bf16 output, +0) in fp32,
+            // rounded once (the +0 start of the reduce's sum decides the sign
+            // of zero); the other rows go to O. One store either way, through
+            // a per-lane address; rows past the segment store nothing.
+            const bool to_y = yrow[i] >= 0;
+            u32x4 v = out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t yv =
+                  pack_bf16x2_hw(__builtin_fmaf(ywt[i], __uint_as_float(out[e] << 16), 0.0f),
+                                 __builtin_fmaf(ywt[i], __uint_as_float(out[e] & 0xffff0000u), 0.0f));
+              v[e] = to_y ? yv : out[e];
+            }
+            const int lrow = wm * 128 + i * 32 + (lane & 31);
+            uint16_t* dst = to_y ? Yb + static_cast<int64_t>(yrow[i]) * a.Nc + col
+                                 : Cb + static_cast<int64_t>(t.row0 + lrow) * a.Nc + col;
+            if (lrow < t.rows_valid) *reinterpret_cast<u32x4*>(dst) = v;
+          }
         }
         // one weight block at a time: the register stages stay live here
         __builtin_amdgcn_sched_barrier(0);
@@ -681,6 +733,7 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
         const int r = off + (xv[q] ? tok : 0);
         xp[q] = Ab + static_cast<int64_t>(a.gather ? a.gather[r] : r) * Kd;
       }
+
       floatx4 acc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
       int kb = kb0;
       for (; kb + kStreamU <= kb1; kb += kStreamU) {
@@ -837,7 +890,8 @@ bool gemm_can_gather(const tr_moe_desc& d) {
 }
 
 hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, int parts,
-                        hipStream_t st, const void* x_gather) {
+                        hipStream_t st, const void* x_gather, const float* w_fused,
+                        void* y_fused) {
   const tr_moe_desc& d = p.d;
   if (d.T == 0) return hipSuccess;
   const int cus = device_cu_count();
@@ -848,7 +902,7 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   const bool up = parts & kGemmUp, down = parts & kGemmDown;
   const int64_t a_rows = p.R_cap + kRowPad;
   GemmArgs g1{p.Xe, w1, p.h, p.counts, p.offsets, E, static_cast<int>(d.H), I, mode, a_rows,
-              nullptr};
+              nullptr, nullptr, nullptr, nullptr, d.K, d.T};
   if (x_gather && d.dtype == TR_BF16) {
     // GEMM1 reads the received rows through the route table: no Xe
     g1.A = x_gather;
@@ -856,7 +910,12 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     g1.gather = p.row_src;
   }
   GemmArgs g2{p.h, w2, p.O, p.counts, p.offsets, E, I, static_cast<int>(d.H), mode, a_rows,
-              nullptr};
+              nullptr, nullptr, nullptr, nullptr, d.K, d.T};
+  if (y_fused && d.dtype == TR_BF16) {
+    g2.dst = p.row_dst;
+    g2.wts = w_fused;
+    g2.y = y_fused;
+  }
   hipError_t err;
 
   if (d.dtype == TR_F32) {

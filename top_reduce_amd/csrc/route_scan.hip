@@ -62,8 +62,10 @@ __device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1,
 template <typename IdxT>
 __global__ __launch_bounds__(kThreads) void route_count(const IdxT* __restrict__ idx, int64_t T,
                                                         int K, int64_t eb, int E, int rpb,
-                                                        int* __restrict__ hist) {
+                                                        int* __restrict__ hist,
+                                                        int* __restrict__ stats) {
   extern __shared__ int cnt[];
+  if (blockIdx.x == 0 && threadIdx.x == 0) stats[4] = 0;   // tok_rest entries (route_scatter)
   for (int i = threadIdx.x; i < E + 2; i += kThreads) cnt[i] = 0;
   __syncthreads();
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rpb;
@@ -79,7 +81,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     const IdxT* __restrict__ idx, int64_t T, int K, int64_t eb, int E, int rpb, int nblocks,
     const int* __restrict__ hist, int* __restrict__ counts, int* __restrict__ offsets,
     int* __restrict__ row_map, int* __restrict__ row_src, int* __restrict__ row_k,
-    int* __restrict__ stats) {
+    int* __restrict__ stats, int* __restrict__ row_dst, int* __restrict__ tok_rest,
+    int min_tiled) {
   extern __shared__ int sh[];
   int* base = sh;                       // [E] first row of this block's slots per expert
   int* running = base + E;              // [E] rows taken so far by this block
@@ -97,6 +100,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   for (int i = tid; i < E + 2; i += kThreads) cnt[i] = 0;
   for (int i = tid; i < E; i += kThreads) prior[i] = 0;
   if (tid < 4) misc[tid] = 0;
+  if (kSelf && tid == 0) stats[4] = 0;   // tok_rest entries (phase 3)
   __syncthreads();
   if (kSelf) {
     count_rows(idx, r0, r1, K, eb, E, cnt);
@@ -209,6 +213,38 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
       }
     }
   }
+
+  // 3. destinations for the reduce folded into the tiled GEMM2: the row of a
+  // received row with exactly one local slot, whose expert has at least
+  // min_tiled routes (the experts of the tiled kernel), names that slot;
+  // other rows name none, and their received rows (and the ones with no
+  // local slot) join tok_rest. This block's rows are its own received rows,
+  // so its row_map entries are complete after the barrier; cnt[] holds the
+  // experts' totals.
+  __syncthreads();
+  for (int64_t tb = r0; tb < r1; tb += kThreads) {
+    const int64_t t = tb + tid;
+    bool rest = false;
+    if (t < r1) {
+      int n = 0, k1 = 0;
+      for (int k = 0; k < K; ++k)
+        if (row_map[t * K + k] >= 0) {
+          ++n;
+          k1 = k;
+        }
+      const bool direct = n == 1 && cnt[local_of(idx[t * K + k1], eb, E)] >= min_tiled;
+      for (int k = 0; k < K; ++k) {
+        const int m = row_map[t * K + k];
+        if (m >= 0) row_dst[m] = direct ? static_cast<int>(t * K + k) : -1;
+      }
+      rest = !direct;
+    }
+    const uint64_t mask = __ballot(rest);
+    int at = 0;
+    if (lane_id() == 0 && mask) at = atomicAdd(&stats[4], __popcll(mask));
+    at = __shfl(at, 0);
+    if (rest) tok_rest[at + popc_below(mask)] = static_cast<int>(t);
+  }
 }
 
 template <typename IdxT>
@@ -217,19 +253,23 @@ hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
   const int E = d.E, K = d.K;
   const int nb = p.scan_blocks, rpb = p.scan_rows_per_block;
   const size_t sh_scatter = sizeof(int) * (2 * E + kWaves * (E + 1) + (E + 2) + kWaves + 4);
+  // fewest routes of an expert the grouped GEMM tiles (the others stream)
+  const int min_tiled = (d.flags & TR_FLAG_GEMM_FORCE_STREAM) ? INT32_MAX
+                        : (d.flags & TR_FLAG_GEMM_FORCE_TILED) ? 1 : kStreamMaxRows + 1;
   if (nb == 1) {
+    // one block: its route_scatter zeroes the tok_rest count itself
     hipLaunchKernelGGL((route_scatter<IdxT, true>), dim3(1), dim3(kThreads), sh_scatter, st, idx,
                        d.T, K, d.expert_begin, E, rpb, nb, p.scan_tmp, p.counts, p.offsets,
-                       p.row_map, p.row_src, p.row_k, p.stats);
+                       p.row_map, p.row_src, p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((route_count<IdxT>), dim3(nb), dim3(kThreads), sizeof(int) * (E + 2), st,
-                     idx, d.T, K, d.expert_begin, E, rpb, p.scan_tmp);
+                     idx, d.T, K, d.expert_begin, E, rpb, p.scan_tmp, p.stats);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((route_scatter<IdxT, false>), dim3(nb), dim3(kThreads), sh_scatter, st, idx,
                      d.T, K, d.expert_begin, E, rpb, nb, p.scan_tmp, p.counts, p.offsets,
-                     p.row_map, p.row_src, p.row_k, p.stats);
+                     p.row_map, p.row_src, p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
   return hipGetLastError();
 }
 

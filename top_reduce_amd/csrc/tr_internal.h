@@ -25,12 +25,16 @@ enum { kGemmUp = 1, kGemmDown = 2 };
 // parts: kGemmUp (Xe -> h, SwiGLU), kGemmDown (h -> O), or both. With
 // x_gather (bf16 only), GEMM1 reads the received rows x through the plan's
 // route table instead of Xe, so no expand pass is needed.
+// With y_fused (bf16 only), GEMM2 writes the rows of received rows with one
+// local slot straight to y, weighted (w_fused, NULL for 1) and rounded as the
+// reduce would; combine_reduce with skip_single then completes y.
 hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, int parts,
-                        hipStream_t st, const void* x_gather = nullptr);
+                        hipStream_t st, const void* x_gather = nullptr,
+                        const float* w_fused = nullptr, void* y_fused = nullptr);
 // Whether GEMM1 may gather from x of this shape (32-bit buffer offsets).
 bool gemm_can_gather(const tr_moe_desc& d);
 hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const float* w, void* y,
-                          hipStream_t st);
+                          hipStream_t st, bool skip_single = false);
 // y[t] = sum over j of recv[src[t][j]] (src >= 0 and < n_recv), unit weights.
 hipError_t combine_epilogue(int64_t T, int J, int64_t H, bool bf16, const int* src,
                             const void* recv, int64_t n_recv, void* y, hipStream_t st);
