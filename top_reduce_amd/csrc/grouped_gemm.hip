@@ -490,6 +490,17 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     return s2;
   };
 
+  // reduce folded into GEMM2 (rows of received rows with one local slot go to
+  // y): the slots of this lane's four rows of the current tile. Loaded ahead
+  // of the operand loads so that the first use waits for none of them.
+  const bool fused = !kSwiglu && a.dst != nullptr;
+  int slot_c[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm * 128 + i * 32 + (lane & 31);
+    slot_c[i] = (fused && row < t.rows_valid) ? a.dst[t.row0 + row] : -1;
+  }
+
   Regs r0, r1;
   {
     int k0, k1, k2;
@@ -541,15 +552,19 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     // sends the activations of k-tile kt + 2 to its own stage.
     // (a do-while: nk >= 2, and no zero-trip path for the accumulators; not
     // peeled or unrolled, so there is one copy of the step code)
-    // reduce folded into GEMM2: the slots of this lane's four rows, loaded
-    // here so that they have arrived by the epilogue
-    const bool fused = !kSwiglu && a.dst != nullptr;
-    int slot[4];
+    // reduce folded into GEMM2: the weights of this tile's rows (their slots
+    // were loaded one tile earlier) and the slots of the next tile's, so that
+    // neither load is waited for before its use
+    float ywt[4];
+    int slot_n[4];
     if (fused) {
+      const bool more = L + G < total;
+      const TileInfo tn = tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, more ? L + G : L);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        ywt[i] = (slot_c[i] >= 0 && a.wts) ? a.wts[slot_c[i]] : 1.0f;
         const int row = wm * 128 + i * 32 + (lane & 31);
-        slot[i] = row < t.rows_valid ? a.dst[t.row0 + row] : -1;
+        slot_n[i] = (more && row < tn.rows_valid) ? a.dst[tn.row0 + row] : -1;
       }
     }
 
@@ -586,14 +601,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     const int hi = lane >> 5;
     // reduce folded into GEMM2: each lane's four rows' y row and weight
     int yrow[4];
-    float ywt[4];
     uint16_t* __restrict__ Yb = static_cast<uint16_t*>(a.y);
     if (fused) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        yrow[i] = slot[i] >= 0 ? slot[i] / a.K : -1;
-        ywt[i] = (slot[i] >= 0 && a.wts) ? a.wts[slot[i]] : 1.0f;
-      }
+      for (int i = 0; i < 4; ++i) yrow[i] = slot_c[i] >= 0 ? slot_c[i] / a.K : -1;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -662,6 +673,10 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
         // one weight block at a time: the register stages stay live here
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    if (fused) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) slot_c[i] = slot_n[i];
     }
     if (L + G < total) t = tile_info<kOutCols>(a, pre, cnt_s, off_s, total_m, NT, L + G);
     s0 = s1;
