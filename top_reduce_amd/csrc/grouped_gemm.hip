@@ -957,7 +957,10 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   const int64_t u1 = static_cast<int64_t>(E) * cdiv(I, 8), u2 = static_cast<int64_t>(E) * cdiv(d.H, 16);
   const unsigned gs1 = static_cast<unsigned>(u1 < cus * 8 ? u1 : cus * 8);
   const unsigned gs2 = static_cast<unsigned>(u2 < cus * 8 ? u2 : cus * 8);
-  if (up && mode != kModeStream) {
+  // With at most kStreamMaxRows expanded rows no expert can reach the tiled
+  // kernel in AUTO mode: skip its launch (decode batches).
+  const bool tiled = mode == kModeTiled || (mode == kModeAuto && p.R_cap > kStreamMaxRows);
+  if (up && tiled) {
     if (g1.gather)
       hipLaunchKernelGGL((gemm_tiled<true, true>), dim3(gt1), dim3(kThreads), 0, st, g1, I);
     else
@@ -968,7 +971,7 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     hipLaunchKernelGGL(gemm_stream<true>, dim3(gs1), dim3(kThreads), 0, st, g1, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if (down && mode != kModeStream) {
+  if (down && tiled) {
     hipLaunchKernelGGL((gemm_tiled<false, false>), dim3(gt2), dim3(kThreads), 0, st, g2, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
