@@ -16,8 +16,11 @@
  * The path, per call sequence:
  *   moe_plan     route scan: per-expert counts and segment offsets, and the
  *                stable maps between received slots and expanded rows
- *   moe_forward  = moe_expand + moe_grouped_gemm + moe_combine_reduce (bf16
- *                runs GEMM1 straight from x instead: moe_grouped_gemm_up_x)
+ *   moe_forward  = moe_expand + moe_grouped_gemm + moe_combine_reduce; bf16
+ *                runs the fused forms moe_grouped_gemm_up_x (GEMM1 straight
+ *                from x), moe_grouped_gemm_down_y (GEMM2 writing rows with one
+ *                local slot straight to y) and moe_combine_reduce_multi, with
+ *                the same result bit for bit
  *
  * Conventions for every entry point:
  *  - Pointers named "device" are HIP device (or managed) memory; the others
