@@ -466,9 +466,26 @@ def main():
         # the reduce reads the rows of received rows with several local slots
         # and writes those and the rows without a local slot
         work["combine_reduce"] = ("hbm", (R - n_single) * H * b + (T - n_single) * H * b + 8 * T * K)
+    # A GEMM whose arithmetic intensity (flops per algorithmic byte: the
+    # weights of the non-empty experts plus the activations read and written)
+    # is below the ridge of MFMA peak / HBM peak is bound by streaming its
+    # weights, and is reported in GB/s (decode and DP-padded shapes).
+    n_active = wl.E - n_empty
+    gemm_bytes = {
+        "gemm_up": n_active * 2 * I * H * b + T_loc * H * b + R * I * b,
+        "gemm_down": n_active * H * I * b + R * I * b + R * H * b,
+    }
+    ridge = peak_mm * 1e12 / (PEAK_HBM_GBS * 1e9)
     stages = {"route_scan": {"us": us["route_scan"]}}
     for k, (bound, amount) in work.items():
         t_s = us[k] / 1e6
+        extra = {}
+        if k in gemm_bytes:
+            ai = amount / gemm_bytes[k]
+            extra = {"algorithmic_flops": amount, "algorithmic_bytes": gemm_bytes[k],
+                     "arith_intensity": ai, "ridge": ridge}
+            if ai < ridge:
+                bound, amount = "hbm", gemm_bytes[k]
         if bound == "hbm":
             ach = amount / t_s / 1e9
             stages[k] = {"us": us[k], "bound": "hbm", "achieved": ach, "unit": "GB/s",
@@ -477,6 +494,7 @@ def main():
             ach = amount / t_s / 1e12
             stages[k] = {"us": us[k], "bound": bound, "achieved": ach, "unit": "TFLOP/s",
                          "peak": peak_mm, "frac": ach / peak_mm, "algorithmic_flops": amount}
+        stages[k].update(extra)
     dominant = max(work, key=lambda k: us[k])
     dom = stages[dominant]
     src = {"expand": "expand.hip", "gemm_up": "grouped_gemm.hip", "gemm_down": "grouped_gemm.hip",
@@ -510,6 +528,44 @@ def main():
         result["lowbatch_combine"] = lowbatch_combine(args.steps)
         result["lowbatch_epilogue"] = lowbatch_epilogue(args.steps)
     result["hbm_copy_reference"] = copy_reference(stream)
+    result["buffer_rows_per_s"] = T / (ms_step / 1e3)
+
+    # The HBM-bound stages once more with cold caches: before each launch a
+    # 1 GiB read (a sum, so no dirty lines are left to write back during the
+    # timed launch) evicts L2 and the 256 MB MALL, so the operands come from
+    # HBM.
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+
+    def cold_us(launch, reps: int = 10) -> float:
+        times = []
+        for _ in range(reps):
+            scratch.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        return sorted(times)[len(times) // 2]
+
+    cold = {}
+    if gather:
+        cold["combine_reduce"] = cold_us(lambda: tr.combine_reduce_multi(p, w, y, stream=stream))
+        cold["expand_alone"] = cold_us(lambda: tr.expand(p, x, stream=stream))
+        cold_bytes = {"combine_reduce": work["combine_reduce"][1],
+                      "expand_alone": (T_loc + R) * H * b + 4 * T * K}
+    else:
+        cold["combine_reduce"] = cold_us(lambda: tr.combine_reduce(p, w, y=y, stream=stream))
+        cold["expand"] = cold_us(lambda: tr.expand(p, x, stream=stream))
+        cold_bytes = {"combine_reduce": work["combine_reduce"][1], "expand": work["expand"][1]}
+    result["cold"] = {k: {"us": v, "achieved": cold_bytes[k] / v / 1e3, "unit": "GB/s",
+                          "peak": PEAK_HBM_GBS, "frac": cold_bytes[k] / v / 1e3 / PEAK_HBM_GBS,
+                          "method": "median of 10 launches, each after reading 1 GiB"}
+                      for k, v in cold.items()}
+    for k, v in result["cold"].items():
+        log(f"[bench] cold {k:15s} {v['us']:10.2f} us  {v['achieved']:9.1f} GB/s  "
+            f"{100 * v['frac']:5.1f}% of peak")
+    del scratch
 
     # Sampled parity and the CPU oracle baseline on a bounded sample.
     if not (args.no_check and args.no_cpu_baseline):
