@@ -134,6 +134,8 @@ def test_fused_down_is_bf16_only_and_checked_on_the_host():
     st.d = tr.make_desc(T=8, K=2, E=4, H=512, I=128)
     assert lib.moe_grouped_gemm_down_y(C.byref(st), fake, None, None, None) == -1
     assert b"y" in lib.moe_last_error()
+    st.d = tr.make_desc(T=150016, K=2, E=2, H=7168, I=128)   # y past 2 GiB
+    assert lib.moe_grouped_gemm_down_y(C.byref(st), fake, None, fake, None) == -2
 
 
 def test_forward_rejects_misaligned_buffers():

@@ -262,3 +262,46 @@ def test_forward_fused_equals_stages(name, flags, T):
         torch.cuda.synchronize()
         assert torch.equal(y_f.view(torch.int16), y_s.view(torch.int16)), "forward != stages"
         assert torch.equal(y_3.view(torch.int16), y_s.view(torch.int16)), "fused stages != stages"
+
+
+def test_forward_past_2gib_x_takes_the_expand_path():
+    """x of more than 2 GiB is beyond the gathering GEMM's 32-bit buffer
+    offsets: moe_forward and moe_grouped_gemm_up_x then expand first and run
+    GEMM1 over Xe, and the reduce covers every row. Same bits as the stages,
+    and the oracle on sampled rows. (150016 rows x 7168 bf16 = 2.15 GB; 2
+    local experts, few routes, so the GEMMs are small.)"""
+    T, K, E, H, I = 150016, 2, 2, 7168, 128
+    say(f"forward past 2 GiB: T={T} H={H}")
+    g = torch.Generator(device="cuda").manual_seed(17)
+    x = torch.randn((T, H), generator=g, device="cuda").to(torch.bfloat16)
+    rng = np.random.default_rng(17)
+    idx = np.full((T, K), -1, np.int64)
+    rows = rng.choice(T, 300, replace=False)
+    idx[rows, 0] = rng.integers(0, E, rows.size)
+    idx[rows[:100], 1] = 1 - idx[rows[:100], 0]
+    w = rng.random((T, K)).astype(np.float32)
+    w1 = (rng.standard_normal((E, 2 * I, H)) / np.sqrt(H)).astype(np.float32)
+    w2 = (rng.standard_normal((E, H, I)) / np.sqrt(I)).astype(np.float32)
+    w1b, w2b = gen.f32_to_bf16_bits(w1), gen.f32_to_bf16_bits(w2)
+    d_idx, d_w, d_w1, d_w2 = dev(idx), dev(w), dev(w1b), dev(w2b)
+    p = tr.plan(d_idx, E=E, H=H, I=I)
+    y_f = tr.forward(p, x, d_w, d_w1, d_w2)
+    tr.expand(p, x)
+    tr.grouped_gemm(p, d_w1, d_w2)
+    y_s = tr.combine_reduce(p, d_w)
+    torch.cuda.synchronize()
+    assert torch.equal(y_f.view(torch.int16), y_s.view(torch.int16))
+    v = p.views()
+    R = int(tr.plan_stats(p)[0])
+    h_ref = v["h"][:R].clone()
+    tr.grouped_gemm_up_x(p, x, d_w1)           # falls back to expand + GEMM1
+    torch.cuda.synchronize()
+    assert torch.equal(v["h"][:R].view(torch.int16), h_ref.view(torch.int16))
+    with pytest.raises(tr.TopReduceError):
+        tr.grouped_gemm_down_y(p, d_w2, d_w, y_f)
+    toks = np.sort(rows[:24])
+    sel = torch.from_numpy(toks).cuda()
+    ref = oracle.forward(host(x[sel]), idx[toks], w[toks], w1b, w2b, E)
+    _assert_close(as_f64(host(y_f[sel])), ref, "bf16", "y (sampled rows)")
+    others = torch.from_numpy(np.setdiff1d(np.arange(T), rows)[:1000]).cuda()
+    assert (host(y_f[others]) == 0).all()
