@@ -70,6 +70,13 @@ typedef enum { TR_IDX_I32 = 0, TR_IDX_I64 = 1 } tr_idx_dtype;
  * flags send every expert to one of them (for testing). */
 #define TR_FLAG_GEMM_FORCE_TILED 0x1
 #define TR_FLAG_GEMM_FORCE_STREAM 0x2
+/* No expanded-row buffer: the workspace holds no Xe (it shrinks by
+ * (T * K + 256) * H * 2 bytes) and the plan's Xe is NULL. Only the forms that
+ * gather from x work: moe_forward, moe_grouped_gemm_up_x and the entry points
+ * that do not touch Xe. moe_expand, moe_grouped_gemm and moe_grouped_gemm_up
+ * return TR_EUNSUPPORTED. Needs bf16 and T * H * 2 < 2^31, else the
+ * descriptor is TR_EUNSUPPORTED. */
+#define TR_FLAG_NO_XE 0x4
 
 typedef struct tr_moe_desc {
     int64_t T;             /* received rows (recv_x rows), >= 0 */
@@ -101,7 +108,8 @@ typedef struct tr_moe_plan {
     int32_t* stats;        /* [5] R, rows with >= 1 local route, ignored slots, empty
                               experts, entries of tok_rest */
     int32_t* scan_tmp;     /* route-scan block partials */
-    void* Xe;              /* [R_cap + 256, H] expanded rows (expert-contiguous) */
+    void* Xe;              /* [R_cap + 256, H] expanded rows (expert-contiguous);
+                              NULL with TR_FLAG_NO_XE */
     void* h;               /* [R_cap + 256, I] silu(gate) * up */
     void* O;               /* [R_cap, H] expert outputs */
     int32_t scan_blocks;

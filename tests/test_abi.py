@@ -138,6 +138,32 @@ def test_fused_down_is_bf16_only_and_checked_on_the_host():
     assert lib.moe_grouped_gemm_down_y(C.byref(st), fake, None, fake, None) == -2
 
 
+def test_no_xe_flag_drops_the_expanded_buffer():
+    lib = tr.load_library()
+    T, K, H = 16384, 8, 7168
+    full = _ws(tr.make_desc(T=T, K=K, E=32, H=H, I=2048))
+    lean = _ws(tr.make_desc(T=T, K=K, E=32, H=H, I=2048, flags=tr.FLAG_NO_XE))
+    assert full - lean == (T * K + 256) * H * 2
+    # the tiled/stream choice still combines with it
+    assert _ws(tr.make_desc(T=64, K=2, E=8, H=256, I=128,
+                            flags=tr.FLAG_NO_XE | tr.FLAG_GEMM_FORCE_TILED)) > 0
+    # only the gathering GEMM1 can run without Xe: bf16 with x under 2 GiB
+    assert _ws(tr.make_desc(T=8, K=2, E=4, H=104, I=72, dtype=torch.float32,
+                            flags=tr.FLAG_NO_XE)) == 0
+    assert b"TR_FLAG_NO_XE" in lib.moe_last_error()
+    assert _ws(tr.make_desc(T=150016, K=2, E=2, H=7168, I=128, flags=tr.FLAG_NO_XE)) == 0
+    assert _ws(tr.make_desc(T=8, K=2, E=4, H=64, I=64, flags=0x8)) == 0
+    # the entry points over Xe refuse such a plan before any launch
+    st = B.PlanStruct()
+    st.d = tr.make_desc(T=64, K=2, E=8, H=256, I=128, flags=tr.FLAG_NO_XE)
+    fake = C.c_void_p(1 << 40)           # never dereferenced: checks fail first
+    st.ws = fake
+    assert lib.moe_expand(C.byref(st), fake, None) == -2
+    assert b"expanded buffer" in lib.moe_last_error()
+    assert lib.moe_grouped_gemm(C.byref(st), fake, fake, None) == -2
+    assert lib.moe_grouped_gemm_up(C.byref(st), fake, None) == -2
+
+
 def test_forward_rejects_misaligned_buffers():
     lib = tr.load_library()
     st = B.PlanStruct()

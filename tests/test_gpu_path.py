@@ -264,6 +264,37 @@ def test_forward_fused_equals_stages(name, flags, T):
         assert torch.equal(y_3.view(torch.int16), y_s.view(torch.int16)), "fused stages != stages"
 
 
+@pytest.mark.parametrize("name,flags,T", [("mid", 0, None), ("mid", tr.FLAG_GEMM_FORCE_TILED, None),
+                                          ("mid", tr.FLAG_GEMM_FORCE_STREAM, None),
+                                          ("mid_small_experts", 0, None), ("c3", 0, 1)])
+def test_forward_without_xe_buffer(name, flags, T):
+    """A plan made with FLAG_NO_XE has a workspace without the expanded rows
+    (smaller by (T*K + 256) * H * 2 bytes, Xe NULL); moe_forward and
+    moe_grouped_gemm_up_x on it give the same bits as on a full plan, and the
+    entry points over Xe refuse it."""
+    say(f"forward without Xe {name} flags={flags} T={T}")
+    wl = gen.make_workload(name, T=T, variant="random" if name == "c3" else "", with_weights=True)
+    d = upload(wl)
+    dt = torch_dtype(wl)
+    p_full = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=dt, flags=flags)
+    p_lean = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=dt, flags=flags | tr.FLAG_NO_XE)
+    assert p_lean.views()["Xe"] is None
+    assert p_full.ws.numel() - p_lean.ws.numel() == (p_full.R_cap + 256) * wl.H * 2
+    y_full = tr.forward(p_full, d["x"], d["w"], d["w1"], d["w2"])
+    y_lean = tr.forward(p_lean, d["x"], d["w"], d["w1"], d["w2"])
+    R = int(tr.plan_stats(p_lean)[0])
+    tr.grouped_gemm_up_x(p_lean, d["x"], d["w1"])
+    tr.grouped_gemm_up_x(p_full, d["x"], d["w1"])
+    torch.cuda.synchronize()
+    assert torch.equal(y_lean.view(torch.int16), y_full.view(torch.int16))
+    assert torch.equal(p_lean.views()["h"][:R].view(torch.int16),
+                       p_full.views()["h"][:R].view(torch.int16))
+    for call in (lambda: tr.expand(p_lean, d["x"]), lambda: tr.grouped_gemm_up(p_lean, d["w1"]),
+                 lambda: tr.grouped_gemm(p_lean, d["w1"], d["w2"])):
+        with pytest.raises(tr.TopReduceError):
+            call()
+
+
 def test_forward_past_2gib_x_takes_the_expand_path():
     """x of more than 2 GiB is beyond the gathering GEMM's 32-bit buffer
     offsets: moe_forward and moe_grouped_gemm_up_x then expand first and run

@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     F32,
     FLAG_GEMM_FORCE_STREAM,
     FLAG_GEMM_FORCE_TILED,
+    FLAG_NO_XE,
     MoePlan,
     TopReduceError,
     combine_epilogue,

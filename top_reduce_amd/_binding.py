@@ -22,6 +22,7 @@ BF16, F32 = 0, 1
 IDX_I32, IDX_I64 = 0, 1
 FLAG_GEMM_FORCE_TILED = 0x1
 FLAG_GEMM_FORCE_STREAM = 0x2
+FLAG_NO_XE = 0x4
 
 _STATUS = {0: "TR_OK", -1: "TR_EINVAL", -2: "TR_EUNSUPPORTED", -3: "TR_EWORKSPACE", -4: "TR_EHIP"}
 
@@ -180,7 +181,8 @@ class MoePlan:
         return self.ws[off:off + nbytes].view(dtype).view(*shape)
 
     def views(self) -> dict:
-        """Views of the plan's device buffers inside the workspace."""
+        """Views of the plan's device buffers inside the workspace (Xe is None
+        for a plan made with FLAG_NO_XE)."""
         d, s = self.desc, self.struct
         dt = _torch_dtype(d.dtype)
         return dict(
@@ -192,7 +194,7 @@ class MoePlan:
             row_dst=self._view(s.row_dst, s.R_cap, torch.int32, (s.R_cap,)),
             tok_rest=self._view(s.tok_rest, d.T, torch.int32, (d.T,)),
             stats=self._view(s.stats, 5, torch.int32, (5,)),
-            Xe=self._view(s.Xe, s.R_cap * d.H, dt, (s.R_cap, d.H)),
+            Xe=None if not s.Xe else self._view(s.Xe, s.R_cap * d.H, dt, (s.R_cap, d.H)),
             h=self._view(s.h, s.R_cap * d.I, dt, (s.R_cap, d.I)),
             O=self._view(s.O, s.R_cap * d.H, dt, (s.R_cap, d.H)),
         )

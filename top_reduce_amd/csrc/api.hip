@@ -40,9 +40,9 @@ tr_status check_desc(const tr_moe_desc* d) {
   if (d->dtype != TR_BF16 && d->dtype != TR_F32) return fail(TR_EINVAL, "unknown dtype %d", d->dtype);
   if (d->idx_dtype != TR_IDX_I32 && d->idx_dtype != TR_IDX_I64)
     return fail(TR_EINVAL, "unknown idx_dtype %d", d->idx_dtype);
-  const int32_t known = TR_FLAG_GEMM_FORCE_TILED | TR_FLAG_GEMM_FORCE_STREAM;
-  if (d->flags & ~known) return fail(TR_EINVAL, "unknown flags 0x%x", d->flags);
-  if ((d->flags & known) == known) return fail(TR_EINVAL, "both GEMM force flags set");
+  const int32_t force = TR_FLAG_GEMM_FORCE_TILED | TR_FLAG_GEMM_FORCE_STREAM;
+  if (d->flags & ~(force | TR_FLAG_NO_XE)) return fail(TR_EINVAL, "unknown flags 0x%x", d->flags);
+  if ((d->flags & force) == force) return fail(TR_EINVAL, "both GEMM force flags set");
   // GEMM tiles address one expert's weights with 32-bit element offsets.
   if (d->H > (1 << 22) || d->I > (1 << 22) || 2 * d->H * d->I >= (int64_t(1) << 31))
     return fail(TR_EUNSUPPORTED, "H, I must be <= 2^22 and 2*H*I < 2^31");
@@ -56,6 +56,9 @@ tr_status check_desc(const tr_moe_desc* d) {
   } else {
     if (d->H % 8) return fail(TR_EUNSUPPORTED, "fp32 needs H a multiple of 8 (got %lld)", (long long)d->H);
   }
+  // without an expanded buffer GEMM1 must be able to gather from x
+  if ((d->flags & TR_FLAG_NO_XE) && !tr::gemm_can_gather(*d))
+    return fail(TR_EUNSUPPORTED, "TR_FLAG_NO_XE needs bf16 and T * H * 2 < 2^31");
   return TR_OK;
 }
 
@@ -83,7 +86,7 @@ Layout layout(const tr_moe_desc& d) {
   L.row_dst = take(sizeof(int32_t) * L.R_cap);
   L.tok_rest = take(sizeof(int32_t) * d.T);
   L.scan_tmp = take(sizeof(int32_t) * static_cast<size_t>(L.blocks) * (d.E + 2));
-  L.Xe = take(es * (L.R_cap + tr::kRowPad) * d.H);
+  L.Xe = take((d.flags & TR_FLAG_NO_XE) ? 0 : es * (L.R_cap + tr::kRowPad) * d.H);
   L.h = take(es * (L.R_cap + tr::kRowPad) * d.I);
   L.O = take(es * L.R_cap * d.H);
   L.total = o;
@@ -159,7 +162,7 @@ tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size
   p.row_dst = reinterpret_cast<int32_t*>(b + L.row_dst);
   p.tok_rest = reinterpret_cast<int32_t*>(b + L.tok_rest);
   p.scan_tmp = reinterpret_cast<int32_t*>(b + L.scan_tmp);
-  p.Xe = b + L.Xe;
+  p.Xe = (desc->flags & TR_FLAG_NO_XE) ? nullptr : b + L.Xe;
   p.h = b + L.h;
   p.O = b + L.O;
   p.scan_blocks = L.blocks;
@@ -179,9 +182,17 @@ static tr_status check_buf(const void* p, const char* name, bool needed) {
   return TR_OK;
 }
 
+// The entry points that read or write the expanded buffer.
+static tr_status check_has_xe(const tr_moe_plan* plan, const char* what) {
+  if (plan->d.flags & TR_FLAG_NO_XE)
+    return fail(TR_EUNSUPPORTED, "%s needs the expanded buffer (plan made with TR_FLAG_NO_XE)", what);
+  return TR_OK;
+}
+
 tr_status moe_expand(const tr_moe_plan* plan, const void* x, hipStream_t stream) {
   tr_status s = check_plan(plan);
   if (s != TR_OK) return s;
+  if ((s = check_has_xe(plan, "moe_expand")) != TR_OK) return s;
   const bool any = plan->d.T > 0;
   if ((s = check_buf(x, "x", any)) != TR_OK) return s;
   if (!any) return ok();
@@ -192,6 +203,7 @@ tr_status moe_grouped_gemm(const tr_moe_plan* plan, const void* w1, const void* 
                            hipStream_t stream) {
   tr_status s = check_plan(plan);
   if (s != TR_OK) return s;
+  if ((s = check_has_xe(plan, "moe_grouped_gemm")) != TR_OK) return s;
   const bool any = plan->d.T > 0;
   if ((s = check_buf(w1, "w1", any)) != TR_OK) return s;
   if ((s = check_buf(w2, "w2", any)) != TR_OK) return s;
@@ -203,6 +215,7 @@ tr_status moe_grouped_gemm(const tr_moe_plan* plan, const void* w1, const void* 
 tr_status moe_grouped_gemm_up(const tr_moe_plan* plan, const void* w1, hipStream_t stream) {
   tr_status s = check_plan(plan);
   if (s != TR_OK) return s;
+  if ((s = check_has_xe(plan, "moe_grouped_gemm_up")) != TR_OK) return s;
   const bool any = plan->d.T > 0;
   if ((s = check_buf(w1, "w1", any)) != TR_OK) return s;
   if (!any) return ok();
