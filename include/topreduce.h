@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define TR_ABI_VERSION 3
+#define TR_ABI_VERSION 4
 
 typedef enum {
     TR_OK = 0,
@@ -105,8 +105,9 @@ typedef struct tr_moe_plan {
     int32_t* row_map;      /* [T*K] expanded row of slot (t,k), or -1 */
     int32_t* row_src;      /* [R_cap] received row of expanded row r (r < R) */
     int32_t* row_k;        /* [R_cap] slot of expanded row r (r < R) */
-    int32_t* stats;        /* [5] R, rows with >= 1 local route, ignored slots, empty
-                              experts, entries of tok_rest */
+    int32_t* stats;        /* [6] R, rows with >= 1 local route, ignored slots, empty
+                              experts, entries of tok_rest, rows that carry a
+                              token (T, or the carrying rows of a padded plan) */
     int32_t* scan_tmp;     /* route-scan block partials */
     void* Xe;              /* [R_cap + 256, H] expanded rows (expert-contiguous);
                               NULL with TR_FLAG_NO_XE */
@@ -120,6 +121,9 @@ typedef struct tr_moe_plan {
                               moe_grouped_gemm_down_y), else -1 */
     int32_t* tok_rest;     /* [T] the other received rows, in no particular order;
                               stats[4] of them */
+    int32_t block_rows;    /* moe_plan_padded: rows per worker block; 0 otherwise */
+    int32_t reserved2;
+    const int32_t* block_counts;  /* moe_plan_padded: the caller's block_counts */
 } tr_moe_plan;
 
 /* Bytes of device workspace a plan for `desc` needs (every buffer above,
@@ -135,6 +139,44 @@ size_t moe_workspace_size(const tr_moe_desc* desc);
  * topk_idx may be freed once the stream has passed this call. */
 tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size_t ws_bytes,
                    hipStream_t stream, tr_moe_plan* out);
+
+/* Route scan of a DP-padded received buffer (SGLang PR #6092: data-parallel
+ * workers of different batch sizes share one FFN input of fixed shape, each
+ * worker's rows padded to the largest batch; padded rows hold no query and
+ * must cost no expert work). The T rows are split into blocks of block_rows
+ * rows (the last block may be shorter), one per worker; the first
+ * block_counts[j] rows of block j carry tokens and the rest are padding.
+ * Padding rows are rows without a local slot whatever topk_idx holds there
+ * (their ids are never read): they get no expanded row and no GEMM work,
+ * their row_map entries are -1, they count in none of stats[0..2], and the
+ * forward writes them as +0. Otherwise exactly moe_plan, which is this call
+ * with every row carrying. block_counts: device int32
+ * [ceil(T / block_rows)], each value clamped to [0, block_rows]; read by the
+ * scan only (it may change after the stream has passed this call, but then
+ * moe_compact_rows must be given the same counts). block_rows >= 1 and at
+ * most 4096 blocks, else TR_EUNSUPPORTED. */
+tr_status moe_plan_padded(const tr_moe_desc* desc, const void* topk_idx, int32_t block_rows,
+                          const int32_t* block_counts, void* ws, size_t ws_bytes,
+                          hipStream_t stream, tr_moe_plan* out);
+
+/* Compaction of a DP-padded buffer (SGLang PR #6092, answer: only each
+ * worker's effective rows are copied into the communication buffer, never the
+ * padding). Rows are row_bytes bytes; the T padded rows form blocks of
+ * block_rows rows whose first block_counts[j] rows (clamped to
+ * [0, block_rows]) carry data, and the compact order is block by block, row
+ * order inside a block. to_padded == 0: compact row i = the i-th carrying
+ * padded row, for every carrying row (padded -> compact, as before the
+ * all-gather). to_padded == 1: the reverse, carrying padded row = its compact
+ * row; padding rows are left untouched (compact -> padded, handing each
+ * worker its rows back). n_out: device int32 or NULL; receives the number of
+ * carrying rows. src: device [T or compact rows, row_bytes]; dst likewise;
+ * no overlap. row_bytes a positive multiple of 4 with src and dst 4-byte
+ * aligned (16-byte copies when row_bytes and both pointers allow); at most
+ * 4096 blocks; T == 0 writes only n_out. Bit copies: works for x, topk_idx
+ * and topk_weights alike. */
+tr_status moe_compact_rows(int64_t T, int32_t block_rows, const int32_t* block_counts,
+                           int64_t row_bytes, const void* src, void* dst, int32_t to_padded,
+                           int32_t* n_out, hipStream_t stream);
 
 /* Whole layer: y[t] = sum over local slots k (ascending) of
  * topk_weights[t][k] * MLP_e(x[t]), with MLP_e(x) = W2[e] (silu(W1[e][0:I] x) *

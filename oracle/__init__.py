@@ -38,6 +38,12 @@ def _load():
     lib.oracle_route.restype = C.c_int64
     lib.oracle_route.argtypes = [C.c_int64, C.c_int32, C.c_int64, C.c_int32, _i64p,
                                  _i32p, _i32p, _i32p, _i32p, _i32p]
+    lib.oracle_route_padded.restype = C.c_int64
+    lib.oracle_route_padded.argtypes = [C.c_int64, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
+                                        _i32p, _i64p, _i32p, _i32p, _i32p, _i32p, _i32p]
+    lib.oracle_compact_rows.restype = C.c_int64
+    lib.oracle_compact_rows.argtypes = [C.c_int64, C.c_int32, _i32p, C.c_int64, C.c_void_p,
+                                        C.c_void_p, C.c_int32]
     lib.oracle_expand.restype = None
     lib.oracle_expand.argtypes = [C.c_int64, C.c_int64, C.c_int32, C.c_void_p, _i32p, C.c_void_p]
     lib.oracle_expert_mlp.restype = None
@@ -85,20 +91,50 @@ def silu(z: float) -> float:
     return float(_load().oracle_silu(float(z)))
 
 
-def route(idx: np.ndarray, E: int, expert_begin: int = 0):
-    """Returns dict(counts, offsets, row_map [T,K], row_src [R], row_k [R], R)."""
+def route(idx: np.ndarray, E: int, expert_begin: int = 0, block_rows: int = 0,
+          block_counts: Optional[np.ndarray] = None):
+    """Returns dict(counts, offsets, row_map [T,K], row_src [R], row_k [R], R).
+
+    block_rows > 0: a padded buffer whose block j carries queries in its
+    first block_counts[j] rows only (SGLang PR #6092)."""
     idx = np.ascontiguousarray(idx, dtype=np.int64)
     T, K = idx.shape
+    if block_rows:
+        bc = np.ascontiguousarray(block_counts, dtype=np.int32)
+        assert bc.shape == (-(-T // block_rows),)
+    else:
+        bc = np.zeros(1, np.int32)
     counts = np.zeros(E, np.int32)
     offsets = np.zeros(E + 1, np.int32)
     row_map = np.zeros(T * K, np.int32)
     cap = max(T * K, 1)
     row_src = np.full(cap, -1, np.int32)
     row_k = np.full(cap, -1, np.int32)
-    R = _load().oracle_route(T, K, expert_begin, E, idx.reshape(-1), counts, offsets, row_map,
-                             row_src, row_k)
+    R = _load().oracle_route_padded(T, K, expert_begin, E, int(block_rows), bc, idx.reshape(-1),
+                                    counts, offsets, row_map, row_src, row_k)
     return dict(counts=counts, offsets=offsets, row_map=row_map.reshape(T, K),
                 row_src=row_src[:R].copy(), row_k=row_k[:R].copy(), R=int(R))
+
+
+def compact_rows(src: np.ndarray, block_rows: int, block_counts: np.ndarray,
+                 to_padded: bool = False, dst: Optional[np.ndarray] = None):
+    """Carrying rows of a padded buffer in compact order (to_padded False:
+    returns (compact array of n rows, n)), or compact rows written back into a
+    copy of the padded dst (to_padded True: returns (that copy, n))."""
+    src = np.ascontiguousarray(src)
+    bc = np.ascontiguousarray(block_counts, dtype=np.int32)
+    if to_padded:
+        out = np.array(dst, copy=True, order="C")
+        T = out.shape[0]
+    else:
+        T = src.shape[0]
+        out = np.zeros_like(src)
+    row_bytes = int(np.prod(src.shape[1:], dtype=np.int64)) * src.itemsize
+    assert bc.shape == (-(-T // block_rows),) and out.dtype == src.dtype
+    n = _load().oracle_compact_rows(T, int(block_rows), bc, row_bytes,
+                                    src.ctypes.data_as(C.c_void_p),
+                                    out.ctypes.data_as(C.c_void_p), 1 if to_padded else 0)
+    return (out, int(n)) if to_padded else (out[:n].copy(), int(n))
 
 
 def expand(x: np.ndarray, row_src: np.ndarray) -> np.ndarray:

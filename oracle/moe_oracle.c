@@ -19,6 +19,11 @@
  *    all -1 routes and zero weights; combine without weights is a plain sum).
  *  - The expert MLP form is a reading: the pages say only "group gemm based
  *    MLP"; it is taken as SwiGLU with W1's first I rows the gate, no bias.
+ *  - SGLang PR #6092, review thread: data-parallel workers of unequal batch
+ *    sizes share one FFN input buffer, each worker's rows padded to a common
+ *    size; padded rows hold no query (sequence length 0) and cost no
+ *    computation, and only each worker's effective rows are copied into the
+ *    communication buffer.
  */
 #include "moe_oracle.h"
 
@@ -61,14 +66,31 @@ static int local_expert(int64_t id, int64_t expert_begin, int32_t E) {
     return (e >= 0 && e < (int64_t)E) ? (int)e : -1;
 }
 
-int64_t oracle_route(int64_t T, int32_t K, int64_t expert_begin, int32_t E,
-                     const int64_t* idx, int32_t* counts, int32_t* offsets,
-                     int32_t* row_map, int32_t* row_src, int32_t* row_k) {
+/* Rows of a padded buffer: block j = t / B holds rows [j B, j B + B); its
+ * first block_counts[j] rows carry a query. B == 0: no padding, every row
+ * carries. */
+static int carries_row(int64_t t, int32_t B, const int32_t* block_counts) {
+    if (B == 0) return 1;
+    int64_t j = t / B;
+    return t - j * B < (int64_t)block_counts[j];
+}
+
+/* Local expert of slot (t, k), or -1; a padding row has no local slot. */
+static int slot_expert(int64_t t, int32_t k, int32_t K, int64_t expert_begin, int32_t E,
+                       const int64_t* idx, int32_t B, const int32_t* block_counts) {
+    if (!carries_row(t, B, block_counts)) return -1;
+    return local_expert(idx[t * K + k], expert_begin, E);
+}
+
+int64_t oracle_route_padded(int64_t T, int32_t K, int64_t expert_begin, int32_t E,
+                            int32_t B, const int32_t* block_counts, const int64_t* idx,
+                            int32_t* counts, int32_t* offsets, int32_t* row_map,
+                            int32_t* row_src, int32_t* row_k) {
     /* 1. per-expert route counts */
     for (int32_t e = 0; e < E; ++e) counts[e] = 0;
     for (int64_t t = 0; t < T; ++t)
         for (int32_t k = 0; k < K; ++k) {
-            int e = local_expert(idx[t * K + k], expert_begin, E);
+            int e = slot_expert(t, k, K, expert_begin, E, idx, B, block_counts);
             if (e >= 0) counts[e] += 1;
         }
     /* 2. segment starts: exclusive prefix sum; offsets[E] = R */
@@ -79,7 +101,7 @@ int64_t oracle_route(int64_t T, int32_t K, int64_t expert_begin, int32_t E,
     int32_t* fill = (int32_t*)calloc((size_t)(E > 0 ? E : 1), sizeof(int32_t));
     for (int64_t t = 0; t < T; ++t)
         for (int32_t k = 0; k < K; ++k) {
-            int e = local_expert(idx[t * K + k], expert_begin, E);
+            int e = slot_expert(t, k, K, expert_begin, E, idx, B, block_counts);
             if (e < 0) {
                 row_map[t * K + k] = -1;
                 continue;
@@ -92,6 +114,29 @@ int64_t oracle_route(int64_t T, int32_t K, int64_t expert_begin, int32_t E,
         }
     free(fill);
     return E > 0 ? (int64_t)offsets[E] : 0;
+}
+
+int64_t oracle_route(int64_t T, int32_t K, int64_t expert_begin, int32_t E,
+                     const int64_t* idx, int32_t* counts, int32_t* offsets,
+                     int32_t* row_map, int32_t* row_src, int32_t* row_k) {
+    return oracle_route_padded(T, K, expert_begin, E, 0, NULL, idx, counts, offsets, row_map,
+                               row_src, row_k);
+}
+
+int64_t oracle_compact_rows(int64_t T, int32_t B, const int32_t* block_counts,
+                            int64_t row_bytes, const void* src, void* dst, int32_t to_padded) {
+    /* the carrying rows, block by block, in row order: the n-th of them is
+     * compact row n */
+    int64_t n = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        if (!carries_row(t, B, block_counts)) continue;
+        if (to_padded)
+            memcpy((char*)dst + t * row_bytes, (const char*)src + n * row_bytes, (size_t)row_bytes);
+        else
+            memcpy((char*)dst + n * row_bytes, (const char*)src + t * row_bytes, (size_t)row_bytes);
+        n += 1;
+    }
+    return n;
 }
 
 void oracle_expand(int64_t R, int64_t H, int32_t eb, const void* x,

@@ -40,6 +40,25 @@ int64_t oracle_route(int64_t T, int32_t K, int64_t expert_begin, int32_t E,
                      const int64_t* idx, int32_t* counts, int32_t* offsets,
                      int32_t* row_map, int32_t* row_src, int32_t* row_k);
 
+/* Route table of a padded buffer (SGLang PR #6092: DP workers' rows padded
+ * to one size; padding rows hold no query). Rows form blocks of B rows; row t
+ * carries a query when t - (t / B) B < block_counts[t / B], and the slots of
+ * the other rows are not local whatever idx holds. B == 0: every row carries
+ * (oracle_route). */
+int64_t oracle_route_padded(int64_t T, int32_t K, int64_t expert_begin, int32_t E,
+                            int32_t B, const int32_t* block_counts, const int64_t* idx,
+                            int32_t* counts, int32_t* offsets, int32_t* row_map,
+                            int32_t* row_src, int32_t* row_k);
+
+/* Compaction of a padded buffer (SGLang PR #6092: only the effective rows go
+ * to the communication buffer). The carrying rows (as in oracle_route_padded,
+ * B >= 1), in row order, are compact rows 0, 1, ...; to_padded == 0 copies
+ * each into its compact row of dst, to_padded == 1 copies compact row n of
+ * src back to its padded row of dst (other dst rows untouched). Rows are
+ * row_bytes bytes. Returns the number of carrying rows. */
+int64_t oracle_compact_rows(int64_t T, int32_t B, const int32_t* block_counts,
+                            int64_t row_bytes, const void* src, void* dst, int32_t to_padded);
+
 /* Expand: Xe[r] = x[row_src[r]] for r < R, a bit copy of elem_bytes-wide
  * elements. */
 void oracle_expand(int64_t R, int64_t H, int32_t elem_bytes, const void* x,

@@ -27,7 +27,7 @@ def test_header_declares_entry_points():
     for n in ("moe_workspace_size", "moe_plan", "moe_forward", "moe_expand", "moe_grouped_gemm",
               "moe_combine_reduce", "moe_plan_stats", "moe_grouped_gemm_up", "moe_grouped_gemm_down",
               "moe_combine_epilogue", "moe_grouped_gemm_up_x", "moe_grouped_gemm_down_y",
-              "moe_combine_reduce_multi", "moe_last_error",
+              "moe_combine_reduce_multi", "moe_plan_padded", "moe_compact_rows", "moe_last_error",
               "moe_abi_version"):
         assert n in names
 
@@ -162,6 +162,40 @@ def test_no_xe_flag_drops_the_expanded_buffer():
     assert b"expanded buffer" in lib.moe_last_error()
     assert lib.moe_grouped_gemm(C.byref(st), fake, fake, None) == -2
     assert lib.moe_grouped_gemm_up(C.byref(st), fake, None) == -2
+
+
+def test_padded_plan_and_compaction_check_arguments_on_the_host():
+    lib = tr.load_library()
+    d = tr.make_desc(T=960, K=8, E=32, H=256, I=128)
+    st = B.PlanStruct()
+    need = _ws(d)
+    fake = C.c_void_p(1 << 40)           # never dereferenced: checks fail first
+    assert lib.moe_plan_padded(C.byref(d), fake, 0, fake, fake, need, None, C.byref(st)) == -1
+    assert b"block_rows" in lib.moe_last_error()
+    assert lib.moe_plan_padded(C.byref(d), fake, 120, None, fake, need, None, C.byref(st)) == -1
+    assert b"block_counts" in lib.moe_last_error()
+    mis = C.c_void_p((1 << 40) + 2)
+    assert lib.moe_plan_padded(C.byref(d), fake, 120, mis, fake, need, None, C.byref(st)) == -1
+    # at most 4096 blocks
+    big = tr.make_desc(T=4097, K=1, E=4, H=256, I=128)
+    assert lib.moe_plan_padded(C.byref(big), fake, 1, fake, fake, _ws(big), None,
+                               C.byref(st)) == -2
+    assert lib.moe_plan_padded(C.byref(d), fake, 120, fake, fake, need - 1, None,
+                               C.byref(st)) == -3
+    # compaction
+    cr = lib.moe_compact_rows
+    assert cr(-1, 1, fake, 16, fake, fake, 0, None, None) == -1
+    assert cr(8, 0, fake, 16, fake, fake, 0, None, None) == -1
+    assert cr(8, 4, fake, 6, fake, fake, 0, None, None) == -1          # row bytes % 4
+    assert b"row_bytes" in lib.moe_last_error()
+    assert cr(8, 4, fake, 0, fake, fake, 0, None, None) == -1
+    assert cr(8, 4, fake, 16, fake, fake, 2, None, None) == -1
+    assert cr(8, 4, None, 16, fake, fake, 0, None, None) == -1
+    assert cr(8, 4, fake, 16, None, fake, 0, None, None) == -1
+    assert cr(8, 4, fake, 16, fake, mis, 0, None, None) == -1
+    assert cr(8, 4, fake, 16, fake, fake, 0, mis, None) == -1
+    assert cr(4097, 1, fake, 16, fake, fake, 0, None, None) == -2
+    assert cr(0, 4, None, 16, None, None, 0, None, None) == 0         # nothing to do
 
 
 def test_forward_rejects_misaligned_buffers():

@@ -412,3 +412,82 @@ def test_sglang6092_real_rows_in_padded_buffer():
     wl = gen.make_workload("c4")
     assert wl.T == g["padded_rows"] == 120 * g["workers"]
     assert int(wl.real.sum()) == g["real_rows"] == sum(g["worker_batch"])
+
+
+# --------------------------------------------------------------------------
+# DP-padded buffers (SGLang PR #6092 review thread)
+# --------------------------------------------------------------------------
+
+def _carrying(T, B, counts):
+    """Rows that hold a query, listed block by block: the first counts[j]
+    rows of block j (a count past the block's end means all of it)."""
+    rows = []
+    for j in range(-(-T // B)):
+        for t in range(j * B, min(j * B + B, T)):
+            if t - j * B < counts[j]:
+                rows.append(t)
+    return rows
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_route_padded_brute_force(oracle_mod, case):
+    # catches: block index and in-block offset swapped, <= for <, pad slots
+    # counted, a count past the block's end spilling into the next block
+    rng = np.random.default_rng(rng_seed + 500 + case)
+    T = int(rng.integers(0, 13))
+    K = int(rng.integers(1, 4))
+    E = int(rng.integers(1, 5))
+    B = int(rng.integers(1, 5))
+    nb = -(-T // B)
+    counts = rng.integers(-1, B + 2, size=nb).astype(np.int32)
+    idx = rng.integers(-2, E + 2, size=(T, K))
+    r = oracle_mod.route(idx, E, 0, block_rows=B, block_counts=counts)
+    keep = _carrying(T, B, counts)
+    masked = -np.ones_like(idx)
+    masked[keep] = idx[keep]
+    row_map, cnt, src, ks = _route_by_sort(masked, E, 0)
+    assert np.array_equal(r["row_map"], row_map)
+    assert np.array_equal(r["counts"], cnt)
+    assert r["row_src"].tolist() == src and r["row_k"].tolist() == ks
+
+
+def test_route_padded_full_blocks_is_plain_route(oracle_mod):
+    # every row carries: identical to the plain route table
+    rng = np.random.default_rng(rng_seed + 600)
+    idx = rng.integers(-1, 6, size=(37, 3))
+    a = oracle_mod.route(idx, 6)
+    b = oracle_mod.route(idx, 6, block_rows=8, block_counts=np.full(5, 8, np.int32))
+    c = oracle_mod.route(idx, 6, block_rows=8, block_counts=np.full(5, 1000, np.int32))
+    for r in (b, c):
+        assert r["R"] == a["R"] and np.array_equal(r["row_map"], a["row_map"])
+        assert np.array_equal(r["row_src"], a["row_src"])
+    z = oracle_mod.route(idx, 6, block_rows=8, block_counts=np.zeros(5, np.int32))
+    assert z["R"] == 0 and (z["row_map"] == -1).all()
+
+
+def test_sglang6092_compaction(oracle_mod):
+    # the review thread's batch mix [120, 1, ..., 1] in a 960-row buffer: the
+    # communication buffer holds 127 rows, the real rows of the c4 workload
+    g = load_golden("sglang6092_dp_batch.txt")
+    wl = gen.make_workload("c4")
+    counts = np.array(g["worker_batch"], np.int32)
+    B = g["padded_rows"] // g["workers"]
+    x = wl.x
+    comp, n = oracle_mod.compact_rows(x, B, counts)
+    assert n == g["real_rows"] == comp.shape[0]
+    assert np.array_equal(comp, x[np.nonzero(wl.real)[0]])
+    assert np.array_equal(comp[120], x[120]) and np.array_equal(comp[126], x[840])
+    back, n2 = oracle_mod.compact_rows(comp, B, counts, to_padded=True,
+                                       dst=np.full_like(x, 7))
+    assert n2 == n
+    assert np.array_equal(back[wl.real], x[wl.real]) and (back[~wl.real] == 7).all()
+
+
+def test_compaction_clamps_counts(oracle_mod):
+    # negative counts carry nothing; counts past a block (or the buffer's
+    # end) carry the whole block and nothing more
+    src = np.arange(10 * 2, dtype=np.int32).reshape(10, 2)
+    comp, n = oracle_mod.compact_rows(src, 4, np.array([-3, 9, 5], np.int32))
+    assert n == 6 and comp[:, 0].tolist() == [8, 10, 12, 14, 16, 18]
+    comp, n = oracle_mod.compact_rows(src, 4, np.array([2, 0, 1], np.int32))
+    assert n == 3 and comp[:, 0].tolist() == [0, 2, 16]

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     MoePlan,
     TopReduceError,
     combine_epilogue,
+    compact_rows,
     combine_reduce,
     combine_reduce_multi,
     expand,

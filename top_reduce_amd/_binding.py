@@ -9,6 +9,7 @@ torch uint8 tensor; the library itself allocates nothing.
 from __future__ import annotations
 
 import ctypes as C
+import math
 import os
 from typing import Optional, Tuple
 
@@ -17,7 +18,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libtopreduce.so"
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 BF16, F32 = 0, 1
 IDX_I32, IDX_I64 = 0, 1
 FLAG_GEMM_FORCE_TILED = 0x1
@@ -47,7 +48,8 @@ class PlanStruct(C.Structure):
                 ("scan_tmp", C.c_void_p), ("Xe", C.c_void_p), ("h", C.c_void_p),
                 ("O", C.c_void_p), ("scan_blocks", C.c_int32),
                 ("scan_rows_per_block", C.c_int32), ("row_dst", C.c_void_p),
-                ("tok_rest", C.c_void_p)]
+                ("tok_rest", C.c_void_p), ("block_rows", C.c_int32), ("reserved2", C.c_int32),
+                ("block_counts", C.c_void_p)]
 
 
 _lib = None
@@ -72,6 +74,12 @@ def load_library():
     lib.moe_workspace_size.argtypes = [C.POINTER(Desc)]
     lib.moe_plan.restype = st
     lib.moe_plan.argtypes = [C.POINTER(Desc), vp, vp, C.c_size_t, vp, C.POINTER(PlanStruct)]
+    lib.moe_plan_padded.restype = st
+    lib.moe_plan_padded.argtypes = [C.POINTER(Desc), vp, C.c_int32, vp, vp, C.c_size_t, vp,
+                                    C.POINTER(PlanStruct)]
+    lib.moe_compact_rows.restype = st
+    lib.moe_compact_rows.argtypes = [C.c_int64, C.c_int32, vp, C.c_int64, vp, vp, C.c_int32, vp,
+                                     vp]
     lib.moe_forward.restype = st
     lib.moe_forward.argtypes = [C.POINTER(PlanStruct), vp, vp, vp, vp, vp, vp]
     lib.moe_expand.restype = st
@@ -165,6 +173,7 @@ class MoePlan:
         self.desc = desc
         self.ws = ws
         self.struct = st
+        self.block_counts = None      # moe_plan_padded: the counts it was given
 
     @property
     def T(self):
@@ -193,7 +202,7 @@ class MoePlan:
             row_k=self._view(s.row_k, s.R_cap, torch.int32, (s.R_cap,)),
             row_dst=self._view(s.row_dst, s.R_cap, torch.int32, (s.R_cap,)),
             tok_rest=self._view(s.tok_rest, d.T, torch.int32, (d.T,)),
-            stats=self._view(s.stats, 5, torch.int32, (5,)),
+            stats=self._view(s.stats, 6, torch.int32, (6,)),
             Xe=None if not s.Xe else self._view(s.Xe, s.R_cap * d.H, dt, (s.R_cap, d.H)),
             h=self._view(s.h, s.R_cap * d.I, dt, (s.R_cap, d.I)),
             O=self._view(s.O, s.R_cap * d.H, dt, (s.R_cap, d.H)),
@@ -202,8 +211,15 @@ class MoePlan:
 
 def plan(topk_idx: torch.Tensor, E: int, H: int, I: int, dtype=torch.bfloat16,
          expert_begin: int = 0, flags: int = 0, ws: Optional[torch.Tensor] = None,
-         stream: Optional[torch.cuda.Stream] = None) -> MoePlan:
-    """moe_plan: route scan of topk_idx [T, K] (int32 or int64, global ids or -1)."""
+         stream: Optional[torch.cuda.Stream] = None, block_rows: int = 0,
+         block_counts: Optional[torch.Tensor] = None) -> MoePlan:
+    """moe_plan: route scan of topk_idx [T, K] (int32 or int64, global ids or -1).
+
+    With block_rows > 0 this is moe_plan_padded: the rows form blocks of
+    block_rows rows (one per DP worker) and block j carries tokens in its first
+    block_counts[j] rows only (block_counts: int32 on the GPU, one per block);
+    the other rows are padding whatever their ids. The plan keeps a reference
+    to block_counts."""
     if topk_idx.dim() != 2:
         raise ValueError("topk_idx must be [T, K]")
     if topk_idx.dtype not in (torch.int32, torch.int64):
@@ -217,10 +233,23 @@ def plan(topk_idx: torch.Tensor, E: int, H: int, I: int, dtype=torch.bfloat16,
     _dev_tensor(ws, "ws", torch.uint8)
     idx_ptr = _dev_tensor(topk_idx, "topk_idx") if T > 0 else 0
     st = PlanStruct()
-    _check(load_library().moe_plan(C.byref(desc), C.c_void_p(idx_ptr or None),
-                                   C.c_void_p(ws.data_ptr()), ws.numel(),
-                                   _stream_ptr(stream, dev), C.byref(st)))
-    return MoePlan(desc, ws, st)
+    if block_rows:
+        nb = -(-T // block_rows) if block_rows > 0 else 0
+        if block_counts is None:
+            raise ValueError("block_counts is required with block_rows")
+        bc = _dev_tensor(block_counts, "block_counts", torch.int32, (nb,)) if T > 0 else 0
+        _check(load_library().moe_plan_padded(C.byref(desc), C.c_void_p(idx_ptr or None),
+                                              block_rows, C.c_void_p(bc or None),
+                                              C.c_void_p(ws.data_ptr()), ws.numel(),
+                                              _stream_ptr(stream, dev), C.byref(st)))
+    else:
+        _check(load_library().moe_plan(C.byref(desc), C.c_void_p(idx_ptr or None),
+                                       C.c_void_p(ws.data_ptr()), ws.numel(),
+                                       _stream_ptr(stream, dev), C.byref(st)))
+    mp = MoePlan(desc, ws, st)
+    if block_rows:
+        mp.block_counts = block_counts
+    return mp
 
 
 def _opt_weights(p: MoePlan, topk_weights) -> Optional[int]:
@@ -359,6 +388,41 @@ def combine_epilogue(src: torch.Tensor, recv: torch.Tensor, y: Optional[torch.Te
                                                C.c_void_p(rp or None), N, C.c_void_p(yp or None),
                                                _stream_ptr(stream, recv.device)))
     return y
+
+
+def compact_rows(src: torch.Tensor, block_rows: int, block_counts: torch.Tensor,
+                 dst: Optional[torch.Tensor] = None, to_padded: bool = False,
+                 n_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_compact_rows over the first dimension of src (any dtype, rows of a
+    multiple of 4 bytes). Padded -> compact: dst gets the carrying rows of
+    src [T, ...] (dst allocated with T rows if None; the first n rows hold
+    them). Compact -> padded (to_padded): dst [T, ...] must be given; its
+    carrying rows are overwritten from src and its padding rows left as they
+    are. n_out: int32 [1] on the GPU, receives the carrying-row count."""
+    if src.dim() < 1:
+        raise ValueError("src needs a row dimension")
+    if to_padded:
+        if dst is None:
+            raise ValueError("to_padded needs dst (the padded buffer)")
+        T = dst.shape[0]
+    else:
+        T = src.shape[0]
+        if dst is None:
+            dst = torch.empty_like(src)
+    row_bytes = math.prod(src.shape[1:]) * src.element_size()
+    nb = -(-T // block_rows) if block_rows > 0 else 0
+    bc = _dev_tensor(block_counts, "block_counts", torch.int32, (nb,)) if T > 0 else 0
+    sp = _dev_tensor(src, "src") if src.numel() else 0
+    dp = _dev_tensor(dst, "dst") if dst.numel() else 0
+    if dst.dtype != src.dtype or tuple(dst.shape[1:]) != tuple(src.shape[1:]):
+        raise ValueError("src and dst must have the same dtype and row shape")
+    np_ = _dev_tensor(n_out, "n_out", torch.int32, (1,)) if n_out is not None else 0
+    dev = src.device if src.is_cuda else dst.device
+    _check(load_library().moe_compact_rows(T, block_rows, C.c_void_p(bc or None), row_bytes,
+                                           C.c_void_p(sp or None), C.c_void_p(dp or None),
+                                           1 if to_padded else 0, C.c_void_p(np_ or None),
+                                           _stream_ptr(stream, dev)))
+    return dst
 
 
 def plan_stats(p: MoePlan, stream=None) -> Tuple[int, int, int, int]:

@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libtopreduce.so")
 
-SOURCES = ["api.hip", "route_scan.hip", "expand.hip", "grouped_gemm.hip", "combine_reduce.hip"]
+SOURCES = ["api.hip", "route_scan.hip", "expand.hip", "grouped_gemm.hip", "combine_reduce.hip",
+           "compact.hip"]
 ARCH = os.environ.get("TOP_REDUCE_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

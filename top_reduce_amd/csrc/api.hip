@@ -85,7 +85,7 @@ Layout layout(const tr_moe_desc& d) {
   L.row_k = take(sizeof(int32_t) * L.R_cap);
   L.row_dst = take(sizeof(int32_t) * L.R_cap);
   L.tok_rest = take(sizeof(int32_t) * d.T);
-  L.scan_tmp = take(sizeof(int32_t) * static_cast<size_t>(L.blocks) * (d.E + 2));
+  L.scan_tmp = take(sizeof(int32_t) * static_cast<size_t>(L.blocks) * (d.E + 3));
   L.Xe = take((d.flags & TR_FLAG_NO_XE) ? 0 : es * (L.R_cap + tr::kRowPad) * d.H);
   L.h = take(es * (L.R_cap + tr::kRowPad) * d.I);
   L.O = take(es * L.R_cap * d.H);
@@ -132,8 +132,14 @@ size_t moe_workspace_size(const tr_moe_desc* desc) {
   return layout(*desc).total;
 }
 
-tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size_t ws_bytes,
-                   hipStream_t stream, tr_moe_plan* out) {
+}  // extern "C"
+
+namespace {
+
+// moe_plan with optional padding blocks (B == 0: every row carries a token).
+tr_status plan_rows(const tr_moe_desc* desc, const void* topk_idx, int32_t B,
+                    const int32_t* block_counts, void* ws, size_t ws_bytes, hipStream_t stream,
+                    tr_moe_plan* out) {
   tr_status s = check_desc(desc);
   if (s != TR_OK) return s;
   if (!out) return fail(TR_EINVAL, "out plan is NULL");
@@ -167,12 +173,60 @@ tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size
   p.O = b + L.O;
   p.scan_blocks = L.blocks;
   p.scan_rows_per_block = L.rpb;
+  p.block_rows = B;
+  p.block_counts = block_counts;
   // T == 0 still runs the (one-block) scan so counts, offsets and stats are
   // defined as zeros.
   s = hip_status(tr::route_scan(p, topk_idx, stream), "moe_route_scan launch");
   if (s != TR_OK) return s;
   *out = p;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size_t ws_bytes,
+                   hipStream_t stream, tr_moe_plan* out) {
+  return plan_rows(desc, topk_idx, 0, nullptr, ws, ws_bytes, stream, out);
+}
+
+tr_status moe_plan_padded(const tr_moe_desc* desc, const void* topk_idx, int32_t block_rows,
+                          const int32_t* block_counts, void* ws, size_t ws_bytes,
+                          hipStream_t stream, tr_moe_plan* out) {
+  tr_status s = check_desc(desc);
+  if (s != TR_OK) return s;
+  if (block_rows < 1) return fail(TR_EINVAL, "block_rows must be >= 1 (got %d)", block_rows);
+  if ((desc->T + block_rows - 1) / block_rows > tr::kMaxPadBlocks)
+    return fail(TR_EUNSUPPORTED, "at most %d padding blocks (T / block_rows)", tr::kMaxPadBlocks);
+  if (desc->T > 0 && (!block_counts || !aligned(block_counts, 4)))
+    return fail(TR_EINVAL, "block_counts must be non-NULL and 4-byte aligned");
+  return plan_rows(desc, topk_idx, block_rows, block_counts, ws, ws_bytes, stream, out);
+}
+
+tr_status moe_compact_rows(int64_t T, int32_t block_rows, const int32_t* block_counts,
+                           int64_t row_bytes, const void* src, void* dst, int32_t to_padded,
+                           int32_t* n_out, hipStream_t stream) {
+  if (T < 0) return fail(TR_EINVAL, "T must be >= 0");
+  if (block_rows < 1) return fail(TR_EINVAL, "block_rows must be >= 1 (got %d)", block_rows);
+  if ((T + block_rows - 1) / block_rows > tr::kMaxPadBlocks)
+    return fail(TR_EUNSUPPORTED, "at most %d padding blocks (T / block_rows)", tr::kMaxPadBlocks);
+  if (row_bytes < 4 || row_bytes % 4 != 0 || row_bytes > (int64_t{1} << 40))
+    return fail(TR_EINVAL, "row_bytes must be a positive multiple of 4");
+  if (to_padded != 0 && to_padded != 1) return fail(TR_EINVAL, "to_padded must be 0 or 1");
+  if (n_out && !aligned(n_out, 4)) return fail(TR_EINVAL, "n_out misaligned");
+  if (T > 0) {
+    if (!block_counts || !aligned(block_counts, 4))
+      return fail(TR_EINVAL, "block_counts must be non-NULL and 4-byte aligned");
+    if (!src || !aligned(src, 4) || !dst || !aligned(dst, 4))
+      return fail(TR_EINVAL, "src and dst must be non-NULL and 4-byte aligned");
+  } else if (!n_out) {
+    return ok();
+  }
+  return hip_status(tr::compact_rows(T, block_rows, block_counts, row_bytes, src, dst,
+                                     to_padded != 0, n_out, stream),
+                    "moe_compact_rows launch");
 }
 
 static tr_status check_buf(const void* p, const char* name, bool needed) {

@@ -20,6 +20,9 @@
 //    maps are bit-exact and deterministic.
 //  - a small input (T*K <= 4096) runs as one block that counts for itself:
 //    one launch instead of two.
+//  - a DP-padded buffer (SGLang PR #6092: workers' batches padded to one
+//    shape) names per block of rows how many carry tokens; the other rows are
+//    treated as rows without a local slot, and their ids are never loaded.
 #include "tr_device.h"
 #include "tr_internal.h"
 
@@ -35,15 +38,26 @@ __device__ __forceinline__ int local_of(IdxT id, int64_t eb, int E) {
   return (e >= 0 && e < E) ? static_cast<int>(e) : E;  // E: not local
 }
 
-// Adds the slots of rows [r0, r1) to cnt[0..E+2): per-expert counts, then
-// cnt[E] = ignored slots, cnt[E+1] = rows with at least one local slot.
+// Whether received row r carries a token: every row without padding blocks
+// (B == 0); else the first bc[j] rows of block j (B rows each), so a count
+// above B means all of them and one at or below 0 none.
+__device__ __forceinline__ bool carries(int64_t r, int B, const int* __restrict__ bc) {
+  if (B == 0) return true;
+  const int64_t j = r / B;
+  return r - j * B < bc[j];
+}
+
+// Adds the slots of rows [r0, r1) to cnt[0..E+3): per-expert counts, then
+// cnt[E] = ignored slots, cnt[E+1] = rows with at least one local slot,
+// cnt[E+2] = rows that carry a token. Rows that do not carry one count in
+// none of them.
 template <typename IdxT>
 __device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1, int K,
-                           int64_t eb, int E, int* cnt) {
+                           int64_t eb, int E, int B, const int* __restrict__ bc, int* cnt) {
   const int64_t s0 = r0 * K, s1 = r1 * K;
   for (int64_t base = s0; base < s1; base += kThreads) {
     const int64_t s = base + threadIdx.x;
-    const bool in = s < s1;
+    const bool in = s < s1 && carries(s / K, B, bc);
     const int e = in ? local_of(idx[s], eb, E) : E;
     if (e < E) atomicAdd(&cnt[e], 1);
     const uint64_t ign = __ballot(in && e == E);
@@ -51,35 +65,39 @@ __device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1,
   }
   for (int64_t base = r0; base < r1; base += kThreads) {
     const int64_t r = base + threadIdx.x;
+    const bool in = r < r1 && carries(r, B, bc);
     bool any = false;
-    if (r < r1)
+    if (in)
       for (int k = 0; k < K; ++k) any |= local_of(idx[r * K + k], eb, E) < E;
     const uint64_t m = __ballot(any);
     if (lane_id() == 0 && m) atomicAdd(&cnt[E + 1], __popcll(m));
+    const uint64_t c = __ballot(in);
+    if (lane_id() == 0 && c) atomicAdd(&cnt[E + 2], __popcll(c));
   }
 }
 
 template <typename IdxT>
 __global__ __launch_bounds__(kThreads) void route_count(const IdxT* __restrict__ idx, int64_t T,
-                                                        int K, int64_t eb, int E, int rpb,
+                                                        int K, int64_t eb, int E, int rpb, int B,
+                                                        const int* __restrict__ bc,
                                                         int* __restrict__ hist,
                                                         int* __restrict__ stats) {
   extern __shared__ int cnt[];
   if (blockIdx.x == 0 && threadIdx.x == 0) stats[4] = 0;   // tok_rest entries (route_scatter)
-  for (int i = threadIdx.x; i < E + 2; i += kThreads) cnt[i] = 0;
+  for (int i = threadIdx.x; i < E + 3; i += kThreads) cnt[i] = 0;
   __syncthreads();
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rpb;
   const int64_t r1 = r0 + rpb < T ? r0 + rpb : T;
-  count_rows(idx, r0, r1, K, eb, E, cnt);
+  count_rows(idx, r0, r1, K, eb, E, B, bc, cnt);
   __syncthreads();
-  for (int i = threadIdx.x; i < E + 2; i += kThreads) hist[blockIdx.x * (E + 2) + i] = cnt[i];
+  for (int i = threadIdx.x; i < E + 3; i += kThreads) hist[blockIdx.x * (E + 3) + i] = cnt[i];
 }
 
 // kSelf: single block, counts its own rows instead of reading `hist`.
 template <typename IdxT, bool kSelf>
 __global__ __launch_bounds__(kThreads) void route_scatter(
     const IdxT* __restrict__ idx, int64_t T, int K, int64_t eb, int E, int rpb, int nblocks,
-    const int* __restrict__ hist, int* __restrict__ counts, int* __restrict__ offsets,
+    int B, const int* __restrict__ bc, const int* __restrict__ hist, int* __restrict__ counts, int* __restrict__ offsets,
     int* __restrict__ row_map, int* __restrict__ row_src, int* __restrict__ row_k,
     int* __restrict__ stats, int* __restrict__ row_dst, int* __restrict__ tok_rest,
     int min_tiled) {
@@ -87,8 +105,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   int* base = sh;                       // [E] first row of this block's slots per expert
   int* running = base + E;              // [E] rows taken so far by this block
   int* wcnt = running + E;              // [kWaves][E + 1] per-wave counts of a round
-  int* cnt = wcnt + kWaves * (E + 1);   // [E + 2] own counts (kSelf)
-  int* tmp = cnt + (E + 2);             // [kWaves] scan scratch
+  int* cnt = wcnt + kWaves * (E + 1);   // [E + 3] own counts (kSelf)
+  int* tmp = cnt + (E + 3);             // [kWaves] scan scratch
   int* misc = tmp + kWaves;             // [4]
 
   const int tid = threadIdx.x;
@@ -97,20 +115,20 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   const int64_t r1 = r0 + rpb < T ? r0 + rpb : T;
 
   int* prior = wcnt;                    // [E] phase 1 only; wcnt is zeroed after
-  for (int i = tid; i < E + 2; i += kThreads) cnt[i] = 0;
+  for (int i = tid; i < E + 3; i += kThreads) cnt[i] = 0;
   for (int i = tid; i < E; i += kThreads) prior[i] = 0;
   if (tid < 4) misc[tid] = 0;
   if (kSelf && tid == 0) stats[4] = 0;   // tok_rest entries (phase 3)
   __syncthreads();
   if (kSelf) {
-    count_rows(idx, r0, r1, K, eb, E, cnt);
+    count_rows(idx, r0, r1, K, eb, E, B, bc, cnt);
   } else {
     // totals and this block's prior counts from every block's partials; all
     // threads share the (block, expert) grid so the loads are independent
     const int n = nblocks * E;
     for (int i = tid; i < n; i += kThreads) {
       const int b = i / E, e = i - b * E;
-      const int c = hist[b * (E + 2) + e];
+      const int c = hist[b * (E + 3) + e];
       if (c) {
         atomicAdd(&cnt[e], c);
         if (b < static_cast<int>(blockIdx.x)) atomicAdd(&prior[e], c);
@@ -153,17 +171,20 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     }
   }
   if (blockIdx.x == 0) {
-    // ignored slots and rows with a local route, summed over blocks
+    // ignored slots, rows with a local route and carrying rows, summed
+    // over blocks
     if (kSelf) {
-      if (tid == 0) { misc[1] = cnt[E]; misc[2] = cnt[E + 1]; }
+      if (tid == 0) { misc[1] = cnt[E]; misc[2] = cnt[E + 1]; misc[3] = cnt[E + 2]; }
     } else {
-      int ign = 0, tl = 0;
+      int ign = 0, tl = 0, cr = 0;
       for (int b = tid; b < nblocks; b += kThreads) {
-        ign += hist[b * (E + 2) + E];
-        tl += hist[b * (E + 2) + E + 1];
+        ign += hist[b * (E + 3) + E];
+        tl += hist[b * (E + 3) + E + 1];
+        cr += hist[b * (E + 3) + E + 2];
       }
       if (ign) atomicAdd(&misc[1], ign);
       if (tl) atomicAdd(&misc[2], tl);
+      if (cr) atomicAdd(&misc[3], cr);
     }
   }
   __syncthreads();
@@ -173,6 +194,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     stats[1] = misc[2];
     stats[2] = misc[1];
     stats[3] = misc[0];
+    stats[5] = misc[3];
   }
 
   // 2. stable ranks, one round of kThreads slots at a time.
@@ -181,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   for (int64_t rb = s0; rb < s1; rb += kThreads) {
     const int64_t s = rb + tid;
     const bool in = s < s1;
-    const int e = in ? local_of(idx[s], eb, E) : E;
+    const int e = in && carries(s / K, B, bc) ? local_of(idx[s], eb, E) : E;
     const bool valid = e < E;
     uint64_t peers = __ballot(1);
     for (int b = 0; b < nbits; ++b) {
@@ -252,23 +274,25 @@ hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
   const tr_moe_desc& d = p.d;
   const int E = d.E, K = d.K;
   const int nb = p.scan_blocks, rpb = p.scan_rows_per_block;
-  const size_t sh_scatter = sizeof(int) * (2 * E + kWaves * (E + 1) + (E + 2) + kWaves + 4);
+  const size_t sh_scatter = sizeof(int) * (2 * E + kWaves * (E + 1) + (E + 3) + kWaves + 4);
+  const int B = p.block_rows;
+  const int* bc = p.block_counts;
   // fewest routes of an expert the grouped GEMM tiles (the others stream)
   const int min_tiled = (d.flags & TR_FLAG_GEMM_FORCE_STREAM) ? INT32_MAX
                         : (d.flags & TR_FLAG_GEMM_FORCE_TILED) ? 1 : kStreamMaxRows + 1;
   if (nb == 1) {
     // one block: its route_scatter zeroes the tok_rest count itself
     hipLaunchKernelGGL((route_scatter<IdxT, true>), dim3(1), dim3(kThreads), sh_scatter, st, idx,
-                       d.T, K, d.expert_begin, E, rpb, nb, p.scan_tmp, p.counts, p.offsets,
+                       d.T, K, d.expert_begin, E, rpb, nb, B, bc, p.scan_tmp, p.counts, p.offsets,
                        p.row_map, p.row_src, p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((route_count<IdxT>), dim3(nb), dim3(kThreads), sizeof(int) * (E + 2), st,
-                     idx, d.T, K, d.expert_begin, E, rpb, p.scan_tmp, p.stats);
+  hipLaunchKernelGGL((route_count<IdxT>), dim3(nb), dim3(kThreads), sizeof(int) * (E + 3), st,
+                     idx, d.T, K, d.expert_begin, E, rpb, B, bc, p.scan_tmp, p.stats);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((route_scatter<IdxT, false>), dim3(nb), dim3(kThreads), sh_scatter, st, idx,
-                     d.T, K, d.expert_begin, E, rpb, nb, p.scan_tmp, p.counts, p.offsets,
+                     d.T, K, d.expert_begin, E, rpb, nb, B, bc, p.scan_tmp, p.counts, p.offsets,
                      p.row_map, p.row_src, p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
   return hipGetLastError();
 }

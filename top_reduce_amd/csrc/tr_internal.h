@@ -17,6 +17,8 @@ constexpr int kStreamMaxRows = 32;
 constexpr int kRowPad = 256;
 // bf16 shapes: H a multiple of kColMultiple, I of kColMultiple / 2.
 constexpr int kColMultiple = 256;
+// Most worker blocks of a DP-padded buffer (their counts' prefix sits in LDS).
+constexpr int kMaxPadBlocks = 4096;
 
 hipError_t route_scan(const tr_moe_plan& p, const void* idx, hipStream_t st);
 void route_scan_geometry(int64_t T, int K, int* blocks, int* rows_per_block);
@@ -38,6 +40,11 @@ hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const fl
 // y[t] = sum over j of recv[src[t][j]] (src >= 0 and < n_recv), unit weights.
 hipError_t combine_epilogue(int64_t T, int J, int64_t H, bool bf16, const int* src,
                             const void* recv, int64_t n_recv, void* y, hipStream_t st);
+
+// Rows of a DP-padded buffer that carry data (block j of B rows: its first
+// counts[j], clamped) copied to compact order, or back (to_padded).
+hipError_t compact_rows(int64_t T, int B, const int* counts, int64_t row_bytes, const void* src,
+                        void* dst, bool to_padded, int* n_out, hipStream_t st);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
