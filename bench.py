@@ -246,6 +246,87 @@ def lowbatch_epilogue(reps: int):
     return out
 
 
+def padded_buffers(w1, w2, stream, reps: int = 20):
+    """DP-padded inputs (SGLang PR #6092 review thread): the 960-row buffer of
+    8 workers with batches [120, 1, ..., 1] (c4 routing) whose padding rows
+    hold stale local expert ids, as a router run on zero rows would leave
+    them. Forward time on a plain plan (which routes the stale ids: the
+    padded GEMM input the thread warns about) against moe_plan_padded (padding
+    rows cost nothing); then moe_compact_rows on the same buffer and on a
+    16384-row buffer of 8 workers with halving batch sizes, in GB/s of
+    effective rows read and written. The expert weights are the caller's
+    (same shapes as c4's)."""
+    import numpy as np
+    import torch
+
+    import gen
+    import top_reduce_amd as tr
+
+    dev = torch.device("cuda:0")
+    wl = gen.make_workload("c4")
+    B, counts = gen.C4_WORKER_ROWS, gen.C4_WORKER_COUNTS
+    rng = np.random.default_rng(6092)
+    stale = wl.idx.copy()
+    pads = np.nonzero(~wl.real)[0]
+    stale[pads] = rng.integers(0, wl.E, size=(pads.size, wl.K))
+    idx = torch.from_numpy(stale).to(dev)
+    x = torch.from_numpy(wl.x.view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(wl.weights).to(dev)
+    bc = torch.tensor(counts, dtype=torch.int32, device=dev)
+    y = torch.empty_like(x)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+
+    out = {"workload": "c4 routing, 8 workers x 120 rows, batches [120, 1, 1, 1, 1, 1, 1, 1], "
+                       "padding rows with stale local ids", "unit": "us", "launches": reps}
+    ws = torch.empty(tr.workspace_size(tr.make_desc(wl.T, wl.K, wl.E, wl.H, wl.I)),
+                     dtype=torch.uint8, device=dev)
+
+    def fwd(padded):
+        def run():
+            if padded:
+                q = tr.plan(idx, E=wl.E, H=wl.H, I=wl.I, ws=ws, stream=stream, block_rows=B,
+                            block_counts=bc)
+            else:
+                q = tr.plan(idx, E=wl.E, H=wl.H, I=wl.I, ws=ws, stream=stream)
+            tr.forward(q, x, w, w1, w2, y=y, stream=stream)
+            return q
+        return run
+
+    for name, padded in (("plain_plan", False), ("padded_plan", True)):
+        q = fwd(padded)()
+        R = tr.plan_stats(q)[0]
+        out[name] = {"us": timed(fwd(padded)), "R": R}
+    out["speedup"] = out["plain_plan"]["us"] / out["padded_plan"]["us"]
+
+    def compact_case(src, blocks, cnts):
+        n_eff = int(sum(min(max(c, 0), blocks) for c in cnts))
+        dst = torch.empty_like(src)
+        cb = torch.tensor(cnts, dtype=torch.int32, device=dev)
+        t_us = timed(lambda: tr.compact_rows(src, blocks, cb, dst=dst, stream=stream))
+        amount = 2 * n_eff * src[0].numel() * src.element_size()
+        ach = amount / t_us / 1e3
+        return {"us": t_us, "rows": n_eff, "of_rows": src.shape[0], "bound": "hbm",
+                "achieved": ach, "unit": "GB/s", "peak": PEAK_HBM_GBS, "frac": ach / PEAK_HBM_GBS,
+                "algorithmic_bytes": amount}
+
+    out["compact_c4_x"] = compact_case(x, B, counts)
+    big = torch.ones((16384, wl.H), dtype=torch.bfloat16, device=dev)
+    out["compact_16384"] = compact_case(big, 2048, [2048, 1024, 512, 256, 128, 64, 32, 16])
+    del big
+    log(f"[bench] padded buffers: {out}")
+    return out
+
+
 def copy_reference(stream, nbytes: int = 1 << 30, reps: int = 20):
     """Bandwidth of a plain device copy (torch's elementwise negation, read
     nbytes + write nbytes) on the same GPU in the same run: the practical
@@ -527,6 +608,8 @@ def main():
     if not args.no_lowbatch:
         result["lowbatch_combine"] = lowbatch_combine(args.steps)
         result["lowbatch_epilogue"] = lowbatch_epilogue(args.steps)
+    if not args.no_lowbatch and (wl.E, wl.H, wl.I) == (32, 7168, 2048) and bf16:
+        result["padded_buffers"] = padded_buffers(w1, w2, stream)
     result["hbm_copy_reference"] = copy_reference(stream)
     result["buffer_rows_per_s"] = T / (ms_step / 1e3)
 

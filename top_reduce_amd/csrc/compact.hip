@@ -8,11 +8,12 @@
 // counts[j] rows; compact row i is the i-th carrying row, block by block.
 //
 // HBM-bound copy. Every workgroup first forms the exclusive prefix of the
-// clamped counts in LDS (at most kMaxBlocks of them), so a carrying row finds
-// its compact position without a host sync. Work items are 1 KiB slabs of a
-// row (64 lanes x 16 bytes, or 64 x 4 bytes for rows that are not whole
-// 16-byte vectors), walked with a grid stride; a padding row's slabs cost
-// index arithmetic only, no memory traffic.
+// clamped counts in LDS (at most kMaxPadBlocks of them), so the copy needs no
+// host sync. Waves then walk the compact rows with a grid stride: a wave finds
+// its row's block by binary search over the prefix (wave-uniform, in LDS),
+// loads up to kBatch 1 KiB slabs of the row (64 lanes x 16 bytes, or x 4 bytes
+// for rows that are not whole 16-byte vectors) and stores them. Padding rows
+// are never visited.
 #include "tr_device.h"
 #include "tr_internal.h"
 
@@ -21,6 +22,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPerThread = kMaxPadBlocks / kThreads;
+constexpr int kBatch = 8;   // slabs loaded before they are stored
 
 template <typename V>
 __global__ __launch_bounds__(kThreads) void compact_rows(int64_t T, int B, int nb,
@@ -28,8 +30,7 @@ __global__ __launch_bounds__(kThreads) void compact_rows(int64_t T, int B, int n
                                                          int64_t vpr, const V* __restrict__ src,
                                                          V* __restrict__ dst, int to_padded,
                                                          int* __restrict__ n_out) {
-  __shared__ int pre[kMaxPadBlocks];   // block j: compact position of its first row
-  __shared__ int cnt[kMaxPadBlocks];   // block j: carrying rows
+  __shared__ int pre[kMaxPadBlocks + 1];   // block j: compact position of its first row
   __shared__ int tmp[kThreads / kWave];
   const int tid = threadIdx.x;
   // clamped counts, kPerThread consecutive blocks per thread, then the scan
@@ -53,32 +54,41 @@ __global__ __launch_bounds__(kThreads) void compact_rows(int64_t T, int B, int n
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
     const int j = tid * kPerThread + u;
-    if (j < nb) {
-      pre[j] = run;
-      cnt[j] = local[u];
-    }
+    if (j < nb) pre[j] = run;
     run += local[u];
   }
+  if (tid == 0) pre[nb] = total;
   if (blockIdx.x == 0 && tid == 0 && n_out) *n_out = total;
   __syncthreads();
 
   const int lane = lane_id();
-  const int64_t nslab = (vpr + kWave - 1) / kWave;
-  const int64_t gw = (static_cast<int64_t>(blockIdx.x) * kThreads + tid) / kWave;
+  const int64_t gw = __builtin_amdgcn_readfirstlane(
+      static_cast<int>((static_cast<int64_t>(blockIdx.x) * kThreads + tid) / kWave));
   const int64_t nw = static_cast<int64_t>(gridDim.x) * (kThreads / kWave);
-  const int64_t items = T * nslab;
-  for (int64_t item = gw; item < items; item += nw) {
-    const int64_t t = item / nslab;
-    const int64_t j = t / B;
-    const int64_t r = t - j * B;
-    if (r >= cnt[j]) continue;                       // padding row
-    const int64_t c = pre[j] + r;                    // its compact row
-    const int64_t v = (item - t * nslab) * kWave + lane;
-    if (v >= vpr) continue;
-    if (to_padded)
-      dst[t * vpr + v] = src[c * vpr + v];
-    else
-      dst[c * vpr + v] = src[t * vpr + v];
+  for (int64_t c = gw; c < total; c += nw) {
+    // the block of compact row c: the last j with pre[j] <= c (blocks that
+    // carry nothing share their prefix with the next one, so it carries c)
+    int lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    const int64_t t = static_cast<int64_t>(lo) * B + (c - pre[lo]);
+    const V* s = src + (to_padded ? c : t) * vpr;
+    V* d = dst + (to_padded ? t : c) * vpr;
+    for (int64_t v0 = 0; v0 < vpr; v0 += kBatch * kWave) {
+      V v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = v0 + u * kWave + lane;
+        if (i < vpr) v[u] = s[i];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = v0 + u * kWave + lane;
+        if (i < vpr) d[i] = v[u];
+      }
+    }
   }
 }
 
@@ -87,8 +97,7 @@ hipError_t launch(int64_t T, int B, const int* counts, int64_t row_bytes, const 
                   void* dst, int to_padded, int* n_out, hipStream_t st) {
   const int64_t vpr = row_bytes / static_cast<int64_t>(sizeof(V));
   const int nb = static_cast<int>(cdiv(T, B));
-  const int64_t waves = T * cdiv(vpr, kWave);
-  int64_t blocks = cdiv(waves, kThreads / kWave);
+  int64_t blocks = cdiv(T, kThreads / kWave);   // a wave per row at most
   const int64_t cap = static_cast<int64_t>(device_cu_count()) * 8;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;          // T == 0 still writes n_out
