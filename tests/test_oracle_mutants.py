@@ -29,6 +29,11 @@ MUTANTS = {
                               "            if (row < 0) break;\n            for (int64_t h = 0; h < H; ++h) yt[h] += elem(recv"),
     "epilogue_first_only": ("for (int32_t j = 0; j < J; ++j) {\n            const int32_t row = src[t * J + j];",
                             "for (int32_t j = 0; j < (J > 1 ? J - 1 : J); ++j) {\n            const int32_t row = src[t * J + j];"),
+    "padding_off_by_one": ("return t - j * B < (int64_t)block_counts[j];",
+                           "return t - j * B <= (int64_t)block_counts[j];"),
+    "padding_block_index": ("int64_t j = t / B;\n    return t - j * B", "int64_t j = t % B;\n    return t - j * B"),
+    "compact_reversed": ("memcpy((char*)dst + n * row_bytes, (const char*)src + t * row_bytes",
+                         "memcpy((char*)dst + (T - 1 - t) % (n + 1) * row_bytes, (const char*)src + t * row_bytes"),
 }
 
 
