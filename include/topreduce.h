@@ -16,6 +16,9 @@
  * The path, per call sequence:
  *   moe_plan     route scan: per-expert counts and segment offsets, and the
  *                stable maps between received slots and expanded rows
+ *   moe_plan_padded  the same over a DP-padded buffer whose padding rows
+ *                carry no query; moe_compact_rows copies only the effective
+ *                rows of such a buffer, and back
  *   moe_forward  = moe_expand + moe_grouped_gemm + moe_combine_reduce; bf16
  *                runs the fused forms moe_grouped_gemm_up_x (GEMM1 straight
  *                from x), moe_grouped_gemm_down_y (GEMM2 writing rows with one
@@ -151,7 +154,7 @@ tr_status moe_plan(const tr_moe_desc* desc, const void* topk_idx, void* ws, size
  * their row_map entries are -1, they count in none of stats[0..2], and the
  * forward writes them as +0. Otherwise exactly moe_plan, which is this call
  * with every row carrying. block_counts: device int32
- * [ceil(T / block_rows)], each value clamped to [0, block_rows]; read by the
+ * [ceil(T / block_rows)], each value clamped to [0, rows of the block]; read by the
  * scan only (it may change after the stream has passed this call, but then
  * moe_compact_rows must be given the same counts). block_rows >= 1 and at
  * most 4096 blocks, else TR_EUNSUPPORTED. */
