@@ -527,7 +527,13 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
   Frags f;
   read_frags<0, 0, kSwiglu>(f, g, 0);
 
-  bool first = true;
+  // Whether the next tile's first step may leave this tile's kStores output
+  // stores in flight. vmcnt counts in issue order, so "at most kPieces +
+  // kStores outstanding" covers the activation DMA issued before the stores
+  // only if all kStores were issued after it; the fused stores skip rows past
+  // the segment, so after a partial fused tile the first step waits for the
+  // stores as well.
+  bool stores_in_flight = false;
 #pragma clang loop unroll(disable)
   for (int L = pos; L < total; L += G) {
     {
@@ -568,8 +574,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
       }
     }
 
-    bool after_stores = !first;
-    first = false;
+    bool after_stores = stores_in_flight;
     int kt = 0;
 #pragma clang loop unroll(disable)
     do {
@@ -674,6 +679,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    stores_in_flight = !fused || t.rows_valid == BM;
     if (fused) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) slot_c[i] = slot_n[i];
