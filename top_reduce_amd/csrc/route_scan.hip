@@ -57,7 +57,7 @@ __device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1,
   const int64_t s0 = r0 * K, s1 = r1 * K;
   for (int64_t base = s0; base < s1; base += kThreads) {
     const int64_t s = base + threadIdx.x;
-    const bool in = s < s1 && carries(s / K, B, bc);
+    const bool in = s < s1 && (B == 0 || carries(s / K, B, bc));
     const int e = in ? local_of(idx[s], eb, E) : E;
     if (e < E) atomicAdd(&cnt[e], 1);
     const uint64_t ign = __ballot(in && e == E);
@@ -65,7 +65,7 @@ __device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1,
   }
   for (int64_t base = r0; base < r1; base += kThreads) {
     const int64_t r = base + threadIdx.x;
-    const bool in = r < r1 && carries(r, B, bc);
+    const bool in = r < r1 && (B == 0 || carries(r, B, bc));
     bool any = false;
     if (in)
       for (int k = 0; k < K; ++k) any |= local_of(idx[r * K + k], eb, E) < E;
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   for (int64_t rb = s0; rb < s1; rb += kThreads) {
     const int64_t s = rb + tid;
     const bool in = s < s1;
-    const int e = in && carries(s / K, B, bc) ? local_of(idx[s], eb, E) : E;
+    const int e = in && (B == 0 || carries(s / K, B, bc)) ? local_of(idx[s], eb, E) : E;
     const bool valid = e < E;
     uint64_t peers = __ballot(1);
     for (int b = 0; b < nbits; ++b) {
