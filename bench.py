@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c5", choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--T", type=int, default=None, help="row count override (c3: 1, 2, 4, 8, 64)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=18.0,
                     help="target length of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
