@@ -190,3 +190,41 @@ def test_compact_rows_edge_cases():
                     torch.zeros(0, dtype=torch.int32, device="cuda"), n_out=n)
     torch.cuda.synchronize()
     assert int(n.item()) == 0
+
+
+gen.custom_spec("pad_bf16", T=600, K=8, E=8, G=32, H=512, I=256, zipf_s=0.8, seed=21)
+gen.custom_spec("pad_f32", T=300, K=4, E=6, G=12, H=264, I=72, dtype="f32", zipf_s=0.5, seed=22)
+
+
+@pytest.mark.parametrize("name,flags,idx_dtype", [
+    ("pad_bf16", 0, torch.int64), ("pad_bf16", tr.FLAG_NO_XE, torch.int32),
+    ("pad_bf16", tr.FLAG_GEMM_FORCE_TILED | tr.FLAG_NO_XE, torch.int64),
+    ("pad_f32", 0, torch.int32)])
+def test_padded_forward_small(name, flags, idx_dtype):
+    """Every row compared: a padded plan over rows whose padding holds stale
+    ids gives the plain plan's output on the carrying rows (padding ids
+    cleared) bit for bit, +0 on padding rows, and the oracle's values within
+    tolerance; with and without the expanded buffer, for bf16 and fp32."""
+    say(f"padded forward {name} flags={flags} idx={idx_dtype}")
+    wl = gen.make_workload(name, with_weights=True)
+    B = 64
+    nb = -(-wl.T // B)
+    counts = np.random.default_rng(wl.seed).integers(-3, B + 5, size=nb).astype(np.int32)
+    carry = _carrying_mask(wl.T, B, counts)
+    stale = _stale(wl.idx, carry, wl.E, 3)
+    clean = np.where(carry[:, None], wl.idx, -1)
+    d = upload(wl)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    p_pad = tr.plan(torch.from_numpy(stale).to(idx_dtype).cuda(), E=wl.E, H=wl.H, I=wl.I,
+                    dtype=dt, flags=flags, block_rows=B,
+                    block_counts=torch.from_numpy(counts).cuda())
+    p_plain = tr.plan(torch.from_numpy(clean).cuda(), E=wl.E, H=wl.H, I=wl.I, dtype=dt,
+                      flags=flags & ~tr.FLAG_NO_XE)
+    y_pad = tr.forward(p_pad, d["x"], d["w"], d["w1"], d["w2"])
+    y_plain = tr.forward(p_plain, d["x"], d["w"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    bits = torch.int16 if dt == torch.bfloat16 else torch.int32
+    assert torch.equal(y_pad.view(bits), y_plain.view(bits))
+    assert (y_pad[torch.from_numpy(~carry).cuda()].view(bits) == 0).all()
+    ref = oracle.forward(wl.x, clean, wl.weights, wl.w1, wl.w2, wl.E)
+    assert max_err(as_f64(host(y_pad)), ref) <= tolerance(ref, wl.dtype)
