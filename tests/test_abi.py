@@ -195,6 +195,7 @@ def test_padded_plan_and_compaction_check_arguments_on_the_host():
     assert cr(8, 4, fake, 16, fake, mis, 0, None, None) == -1
     assert cr(8, 4, fake, 16, fake, fake, 0, mis, None) == -1
     assert cr(4097, 1, fake, 16, fake, fake, 0, None, None) == -2
+    assert cr((1 << 31) - 1, 1 << 20, fake, 1 << 40, fake, fake, 0, None, None) == -1
     assert cr(0, 4, None, 16, None, None, 0, None, None) == 0         # nothing to do
 
 

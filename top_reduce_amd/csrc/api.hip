@@ -214,6 +214,8 @@ tr_status moe_compact_rows(int64_t T, int32_t block_rows, const int32_t* block_c
     return fail(TR_EUNSUPPORTED, "at most %d padding blocks (T / block_rows)", tr::kMaxPadBlocks);
   if (row_bytes < 4 || row_bytes % 4 != 0 || row_bytes > (int64_t{1} << 40))
     return fail(TR_EINVAL, "row_bytes must be a positive multiple of 4");
+  if (T > 0 && row_bytes > (int64_t{1} << 62) / T)
+    return fail(TR_EINVAL, "T * row_bytes overflows");
   if (to_padded != 0 && to_padded != 1) return fail(TR_EINVAL, "to_padded must be 0 or 1");
   if (n_out && !aligned(n_out, 4)) return fail(TR_EINVAL, "n_out misaligned");
   if (T > 0) {
