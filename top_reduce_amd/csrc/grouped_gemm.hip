@@ -415,26 +415,49 @@ __device__ __forceinline__ TileSrc<kGather> tile_src(const GemmArgs& a, const Ti
 
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <bool kSwiglu, bool kGather>
-__global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ int pre[kMaxE + 1];
-  __shared__ int tmp[kWavesT];
-  __shared__ int cnt_s[kMaxE], off_s[kMaxE];
+// The experts' counts and segment offsets copied to LDS, and the prefix of
+// their m-tiles (experts of the tiled kernel only); returns the m-tiles.
+__device__ __forceinline__ int gemm_prologue(const GemmArgs& a, int* pre, int* tmp, int* cnt_s,
+                                             int* off_s) {
   for (int e = threadIdx.x; e < a.E; e += kThreads) {
     cnt_s[e] = a.counts[e];
     off_s[e] = a.offsets[e];
   }
-
   const int mode = a.mode;
-  const int total_m = expert_prefix(a.counts, a.E, [mode](int c) {
+  return expert_prefix(a.counts, a.E, [mode](int c) {
     return (c > 0 && !goes_to_stream(c, mode)) ? (c + BM - 1) / BM : 0;
   }, pre, tmp);
+}
+
+// GEMM1 and GEMM2 of one forward in three launches, so that the blocks idle
+// in GEMM1's last, partly filled round compute GEMM2 tiles instead (a launch
+// boundary makes GEMM1's output visible to every XCD):
+//   1. GEMM1 tiles [0, R1), R1 the whole rounds on G blocks;
+//   2. GEMM1 tiles [R1, total1) on the first total1 - R1 blocks, and on the
+//      others GEMM2 tiles [0, n2) of m-tiles whose GEMM1 tiles all lie in
+//      [0, R1) (whole groups of kGroupM m-tiles), about as many per block as
+//      fit in one GEMM1 tile's time (the ratio of the reduction lengths);
+//   3. GEMM2 tiles [n2, total2).
+// n2 as a function of the m-tiles, the tiles per m-tile of each GEMM, that
+// ratio and G; launches 2 and 3 compute it alike.
+__device__ __forceinline__ int early_down_tiles(int total_m, int NT1, int NT2, int ratio, int G) {
+  const int total1 = total_m * NT1;
+  const int R1 = total1 / G * G;
+  const int tail = total1 - R1;
+  if (tail == 0 || R1 == 0 || ratio == 0) return 0;
+  const int m_done = min(R1 / (kGroupM * NT1) * kGroupM, total_m);
+  return min((G - tail) * ratio, m_done * NT2);
+}
+
+// Tiles begin + slot, begin + slot + nslots, ... below end of one GEMM, for
+// this block. pre / cnt_s / off_s: the LDS tables of gemm_prologue.
+template <bool kSwiglu, bool kGather>
+__device__ __forceinline__ void gemm_tiles(const GemmArgs& a, int I, const int* pre,
+                                           const int* cnt_s, const int* off_s, int total_m,
+                                           int begin, int end, int slot, int nslots) {
   constexpr int kOutCols = kSwiglu ? BN / 2 : BN;   // output columns per tile
   const int NT = (a.Nc + kOutCols - 1) / kOutCols;
-  const int total = total_m * NT;
-  if (total == 0) return;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -444,10 +467,12 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
 
   // XCD-aware order: blocks are dealt round-robin to the 8 XCDs; give each
   // XCD a contiguous run of the tile order.
-  const int G = gridDim.x;
-  int pos = blockIdx.x;
-  if ((G & 7) == 0) pos = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  if (pos >= total) return;
+  const int G = nslots;
+  int pos = slot;
+  if ((G & 7) == 0) pos = (slot & 7) * (G >> 3) + (slot >> 3);
+  if (pos >= end - begin) return;
+  pos += begin;
+  const int total = end;
 
   Geo g;
   g.d_dst = wave * 64 * kCpr;
@@ -690,6 +715,55 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I) {
     s2 = src_of(L + 3 * G);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, true));   // loads and DMA past the last tile
+}
+#endif  // __HIP_DEVICE_COMPILE__
+
+enum { kPartAll = 0, kPartWholeRounds = 1, kPartRest = 2 };
+
+// One GEMM: every tile (kPartAll), GEMM1's whole rounds (kPartWholeRounds,
+// launch 1 above) or GEMM2's tiles from n2 on (kPartRest, launch 3; g_split
+// is launch 2's grid).
+template <bool kSwiglu, bool kGather>
+__global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I, int part, int g_split) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ int pre[kMaxE + 1];
+  __shared__ int tmp[kWavesT];
+  __shared__ int cnt_s[kMaxE], off_s[kMaxE];
+  const int total_m = gemm_prologue(a, pre, tmp, cnt_s, off_s);
+  constexpr int kOutCols = kSwiglu ? BN / 2 : BN;
+  const int NT = (a.Nc + kOutCols - 1) / kOutCols;
+  const int total = total_m * NT;
+  if (total == 0) return;
+  int begin = 0, end = total;
+  if (part == kPartWholeRounds) end = total / static_cast<int>(gridDim.x) * static_cast<int>(gridDim.x);
+  if (part == kPartRest)   // GEMM2: Kd = I, Nc = H
+    begin = early_down_tiles(total_m, (a.Kd + BN / 2 - 1) / (BN / 2), NT, a.Nc / a.Kd, g_split);
+  gemm_tiles<kSwiglu, kGather>(a, I, pre, cnt_s, off_s, total_m, begin, end, blockIdx.x,
+                               gridDim.x);
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+// Launch 2 above: GEMM1's last round on the first blocks, early GEMM2 tiles
+// on the others (g1 and g2 share the plan's counts and mode).
+template <bool kGather>
+__global__ __launch_bounds__(kThreads) void gemm_hybrid(GemmArgs g1, GemmArgs g2, int I) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ int pre[kMaxE + 1];
+  __shared__ int tmp[kWavesT];
+  __shared__ int cnt_s[kMaxE], off_s[kMaxE];
+  const int total_m = gemm_prologue(g1, pre, tmp, cnt_s, off_s);
+  const int NT1 = (g1.Nc + BN / 2 - 1) / (BN / 2), NT2 = (g2.Nc + BN - 1) / BN;
+  const int G = gridDim.x;
+  const int total1 = total_m * NT1;
+  const int R1 = total1 / G * G;
+  const int tail = total1 - R1;
+  if (static_cast<int>(blockIdx.x) < tail) {
+    gemm_tiles<true, kGather>(g1, I, pre, cnt_s, off_s, total_m, R1, total1, blockIdx.x, tail);
+  } else {
+    const int n2 = early_down_tiles(total_m, NT1, NT2, g1.Kd / g2.Kd, G);
+    gemm_tiles<false, false>(g2, I, pre, cnt_s, off_s, total_m, 0, n2, blockIdx.x - tail,
+                             G - tail);
+  }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
@@ -966,11 +1040,44 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   // With at most kStreamMaxRows expanded rows no expert can reach the tiled
   // kernel in AUTO mode: skip its launch (decode batches).
   const bool tiled = mode == kModeTiled || (mode == kModeAuto && p.R_cap > kStreamMaxRows);
+  // Both GEMMs with enough tiles for several rounds: three launches, GEMM2
+  // tiles filling GEMM1's last round (see early_down_tiles). The whole-round
+  // and hybrid launches share one grid, which the last one is told.
+  const bool split = up && down && tiled && t1 >= 2 * static_cast<int64_t>(cus);
+  if (split) {
+    const unsigned gsplit = gt1;
+    if (g1.gather)
+      hipLaunchKernelGGL((gemm_tiled<true, true>), dim3(gsplit), dim3(kThreads), 0, st, g1, I,
+                         static_cast<int>(kPartWholeRounds), 0);
+    else
+      hipLaunchKernelGGL((gemm_tiled<true, false>), dim3(gsplit), dim3(kThreads), 0, st, g1, I,
+                         static_cast<int>(kPartWholeRounds), 0);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (mode != kModeTiled) {
+      hipLaunchKernelGGL(gemm_stream<true>, dim3(gs1), dim3(kThreads), 0, st, g1, I);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (g1.gather)
+      hipLaunchKernelGGL((gemm_hybrid<true>), dim3(gsplit), dim3(kThreads), 0, st, g1, g2, I);
+    else
+      hipLaunchKernelGGL((gemm_hybrid<false>), dim3(gsplit), dim3(kThreads), 0, st, g1, g2, I);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL((gemm_tiled<false, false>), dim3(gt2), dim3(kThreads), 0, st, g2, I,
+                       static_cast<int>(kPartRest), static_cast<int>(gsplit));
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (mode != kModeTiled) {
+      hipLaunchKernelGGL(gemm_stream<false>, dim3(gs2), dim3(kThreads), 0, st, g2, I);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
+  }
   if (up && tiled) {
     if (g1.gather)
-      hipLaunchKernelGGL((gemm_tiled<true, true>), dim3(gt1), dim3(kThreads), 0, st, g1, I);
+      hipLaunchKernelGGL((gemm_tiled<true, true>), dim3(gt1), dim3(kThreads), 0, st, g1, I,
+                         static_cast<int>(kPartAll), 0);
     else
-      hipLaunchKernelGGL((gemm_tiled<true, false>), dim3(gt1), dim3(kThreads), 0, st, g1, I);
+      hipLaunchKernelGGL((gemm_tiled<true, false>), dim3(gt1), dim3(kThreads), 0, st, g1, I,
+                         static_cast<int>(kPartAll), 0);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (up && mode != kModeTiled) {
@@ -978,7 +1085,8 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (down && tiled) {
-    hipLaunchKernelGGL((gemm_tiled<false, false>), dim3(gt2), dim3(kThreads), 0, st, g2, I);
+    hipLaunchKernelGGL((gemm_tiled<false, false>), dim3(gt2), dim3(kThreads), 0, st, g2, I,
+                       static_cast<int>(kPartAll), 0);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (down && mode != kModeTiled) {
