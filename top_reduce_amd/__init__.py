@@ -7,6 +7,14 @@ and marshals PyTorch tensors (device memory and streams only) and calls the
 library; every step of the path runs in the library's kernels. There is no
 fallback: if the library is not built, importing the binding's entry points
 raises.
+
+Entry points: ``plan`` (route scan; with ``block_rows``/``block_counts`` over
+a DP-padded buffer), ``forward`` (the whole layer), the stages ``expand``,
+``grouped_gemm`` (``grouped_gemm_up``/``_down``, ``grouped_gemm_up_x``
+gathering x, ``grouped_gemm_down_y`` writing single-slot rows to y),
+``combine_reduce`` / ``combine_reduce_multi``, the cross-rank
+``combine_epilogue``, ``compact_rows`` (effective rows of a padded buffer)
+and ``plan_stats``. ``FLAG_NO_XE`` plans without the expanded-row buffer.
 """
 
 from ._binding import (  # noqa: F401
