@@ -25,6 +25,10 @@ gen.custom_spec("mid_f32", T=300, K=4, E=6, G=12, H=264, I=72, dtype="f32", zipf
 # (the last one 32 rows deep); 288 tiles per GEMM, more than one round of the
 # persistent grid on 256 compute units.
 gen.custom_spec("rounds", T=2080, K=8, E=8, G=8, H=1024, I=512, routing="uniform", seed=10)
+# every row routed to all 8 experts: 17 m-tiles each, GEMM1 544 tiles (two
+# rounds of 256 blocks plus 32), so the forward's hybrid launch runs GEMM1's
+# last round beside early GEMM2 tiles
+gen.custom_spec("split", T=4200, K=8, E=8, G=8, H=2048, I=512, routing="uniform", seed=11)
 
 
 def _assert_close(got, ref, dtype, what):
@@ -239,6 +243,7 @@ def test_up_x_decode(T):
 @pytest.mark.parametrize("name,flags,T", [("mid", 0, None), ("mid", tr.FLAG_GEMM_FORCE_TILED, None),
                                           ("mid", tr.FLAG_GEMM_FORCE_STREAM, None),
                                           ("mid_small_experts", 0, None), ("rounds", 0, None),
+                                          ("split", 0, None),
                                           ("c3", 0, 1), ("c3", 0, 64), ("c4", 0, None),
                                           ("c2", 0, None), ("c5", 0, None)])
 def test_forward_fused_equals_stages(name, flags, T):
