@@ -364,6 +364,9 @@ def main():
     import gen
     import top_reduce_amd as tr
 
+    if not os.path.exists(tr.lib_path()):   # a fresh checkout: build it first
+        from top_reduce_amd import build as hip_build
+        hip_build.build()
     tr.load_library()
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
