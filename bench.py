@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
     ap.add_argument("--loop-only", action="store_true",
                     help="only warmup + timed steps (for profiler runs)")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="only warmup + timed plan + moe_forward steps, as the library runs them "
+                         "(for profiler runs of the forward's own launches)")
     ap.add_argument("--no-lowbatch", action="store_true",
                     help="skip the low-batch combine-reduce measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -401,6 +404,22 @@ def main():
     n_single = int((p.views()["row_dst"][:R] >= 0).sum()) if R else 0
     log(f"[bench] R={R} T_loc={T_loc} real_rows={real_rows} empty_experts={n_empty} "
         f"single_slot_rows={n_single}")
+
+    if args.forward_only:
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(args.steps):
+            step()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        ms = f0.elapsed_time(f1) / args.steps
+        log(f"[bench] {args.steps} forward steps: {ms:.4f} ms/step")
+        print(json.dumps({"metric": METRIC, "value": int(wl.real.sum()) / (ms / 1e3), "unit": "tokens/s",
+                          "ms_per_step": ms, "forward_only": True}), flush=True)
+        return
 
     if args.copy_calibration_mib:
         # A plain elementwise kernel over a known number of bytes: its HBM
