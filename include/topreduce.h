@@ -194,7 +194,9 @@ tr_status moe_compact_rows(int64_t T, int32_t block_rows, const int32_t* block_c
  * T * H * 2 < 2^31 it runs moe_grouped_gemm_up_x, moe_grouped_gemm_down_y and
  * moe_combine_reduce_multi instead (the fused forms of expand and of the
  * reduce): Xe is not written, and O only for received rows with several
- * local slots. */
+ * local slots. With enough tiles for several rounds the two GEMMs run as
+ * three launches (GEMM1's whole rounds; its last round beside GEMM2 tiles of
+ * rows GEMM1 has finished; the rest of GEMM2), with the same result. */
 tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_weights,
                       const void* w1, const void* w2, void* y, hipStream_t stream);
 
