@@ -745,6 +745,13 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I, int pa
 
 // Launch 2 above: GEMM1's last round on the first blocks, early GEMM2 tiles
 // on the others (g1 and g2 share the plan's counts and mode).
+//
+// y may alias x. Early GEMM2 tiles write y only for received rows with one
+// local slot, and that slot lies in an m-tile GEMM1 has already finished, so
+// no GEMM1 tile of this launch reads such a row as one of its own. A GEMM1
+// tile does read row 0 of x for the rows past its segment; if y[0] is being
+// written meanwhile, only those filler rows see it, and their outputs are
+// dropped by the store range check.
 template <bool kGather>
 __global__ __launch_bounds__(kThreads) void gemm_hybrid(GemmArgs g1, GemmArgs g2, int I) {
 #if defined(__HIP_DEVICE_COMPILE__)
