@@ -28,7 +28,9 @@
  * Conventions for every entry point:
  *  - Pointers named "device" are HIP device (or managed) memory; the others
  *    are host memory. The caller allocates and owns every buffer, including
- *    the workspace; the library allocates nothing and keeps no per-call state.
+ *    the workspace; the library allocates nothing and keeps no per-call state
+ *    (moe_forward_noalloc alone works in a workspace the library holds as a
+ *    static device array).
  *  - All work is enqueued on `stream` (NULL: the null stream) and returns
  *    without synchronising, except moe_plan_stats, which waits on `stream`.
  *    Calls are graph-capturable except moe_plan_stats.
@@ -55,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TR_ABI_VERSION 4
+#define TR_ABI_VERSION 5
 
 typedef enum {
     TR_OK = 0,
@@ -268,6 +270,31 @@ tr_status moe_combine_reduce_multi(const tr_moe_plan* plan, const float* topk_we
 tr_status moe_combine_epilogue(int64_t T, int32_t J, int64_t H, tr_dtype dtype,
                                const int32_t* src, const void* recv, int64_t n_recv, void* y,
                                hipStream_t stream);
+
+/* Bytes of the library's own static workspace on each device, used by
+ * moe_forward_noalloc only. */
+#define TR_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. moe_plan
+ * followed by moe_forward, with the workspace taken from a device array the
+ * library holds (TR_NOALLOC_SCRATCH_BYTES per device, from module load until
+ * the process ends) instead of the caller's. The result equals moe_plan +
+ * moe_forward bit for bit. Calls no hipMalloc, hipFree or allocating library
+ * routine.
+ *   desc, topk_idx: as moe_plan; x, topk_weights, w1, w2, y: as moe_forward.
+ *   bf16 plans without the expanded-row buffer (TR_FLAG_NO_XE is added when
+ *   allowed), so the batch fits when moe_workspace_size of that descriptor is
+ *   at most TR_NOALLOC_SCRATCH_BYTES (decode and small prefill batches, e.g.
+ *   T = 64, K = 16, H = 3584, I = 2048 needs about 13 MB); larger batches
+ *   return TR_EUNSUPPORTED before anything is enqueued.
+ * Every call on one device shares that device's array and leaves its last
+ * contents there (nothing in it needs to start zeroed: the route scan writes
+ * every entry the later kernels read). Calls that overlap on one device (two
+ * streams, or two threads, without ordering between them) race on it. */
+tr_status moe_forward_noalloc(const tr_moe_desc* desc, const void* topk_idx, const void* x,
+                              const float* topk_weights, const void* w1, const void* w2,
+                              void* y, hipStream_t stream);
 
 /* Copies stats to host_out[4] = {R, rows with a local route, ignored slots,
  * empty experts} and synchronises `stream` (opt-in host sync, the counterpart

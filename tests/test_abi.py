@@ -28,7 +28,7 @@ def test_header_declares_entry_points():
               "moe_combine_reduce", "moe_plan_stats", "moe_grouped_gemm_up", "moe_grouped_gemm_down",
               "moe_combine_epilogue", "moe_grouped_gemm_up_x", "moe_grouped_gemm_down_y",
               "moe_combine_reduce_multi", "moe_plan_padded", "moe_compact_rows", "moe_last_error",
-              "moe_abi_version"):
+              "moe_abi_version", "moe_forward_noalloc"):
         assert n in names
 
 
@@ -237,3 +237,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_HERE", str(tmp_path))
     with pytest.raises(ImportError):
         B.load_library()
+
+
+def test_noalloc_refuses_batch_past_scratch_on_host():
+    """moe_forward_noalloc checks the batch against its static workspace
+    before it touches a device: a prefill-sized batch is TR_EUNSUPPORTED (no
+    pointer is read), an invalid descriptor TR_EINVAL."""
+    lib = tr.load_library()
+    big = tr.make_desc(T=16384, K=8, E=32, H=7168, I=2048)
+    null = C.c_void_p(None)
+    st = lib.moe_forward_noalloc(C.byref(big), null, null, null, null, null, null, null)
+    assert st == -2
+    assert b"static scratch" in lib.moe_last_error()
+    bad = tr.make_desc(T=64, K=0, E=8, H=256, I=128)
+    assert lib.moe_forward_noalloc(C.byref(bad), null, null, null, null, null, null, null) == -1
+    # the decode batch fits: its descriptor (bf16, no expanded rows) needs
+    # less than the scratch holds
+    dec = tr.make_desc(T=64, K=16, E=28, H=3584, I=2048, flags=tr.FLAG_NO_XE)
+    assert 0 < _ws(dec) <= tr.NOALLOC_SCRATCH_BYTES

@@ -15,6 +15,8 @@ gathering x, ``grouped_gemm_down_y`` writing single-slot rows to y),
 ``combine_reduce`` / ``combine_reduce_multi``, the cross-rank
 ``combine_epilogue``, ``compact_rows`` (effective rows of a padded buffer)
 and ``plan_stats``. ``FLAG_NO_XE`` plans without the expanded-row buffer.
+``forward_noalloc`` is plan + forward in the library's own static workspace,
+for callers that cannot allocate device memory.
 """
 
 from ._binding import (  # noqa: F401
@@ -24,6 +26,7 @@ from ._binding import (  # noqa: F401
     FLAG_GEMM_FORCE_STREAM,
     FLAG_GEMM_FORCE_TILED,
     FLAG_NO_XE,
+    NOALLOC_SCRATCH_BYTES,
     MoePlan,
     TopReduceError,
     combine_epilogue,
@@ -32,6 +35,7 @@ from ._binding import (  # noqa: F401
     combine_reduce_multi,
     expand,
     forward,
+    forward_noalloc,
     grouped_gemm,
     grouped_gemm_down,
     grouped_gemm_down_y,

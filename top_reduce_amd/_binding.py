@@ -18,12 +18,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libtopreduce.so"
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 BF16, F32 = 0, 1
 IDX_I32, IDX_I64 = 0, 1
 FLAG_GEMM_FORCE_TILED = 0x1
 FLAG_GEMM_FORCE_STREAM = 0x2
 FLAG_NO_XE = 0x4
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 _STATUS = {0: "TR_OK", -1: "TR_EINVAL", -2: "TR_EUNSUPPORTED", -3: "TR_EWORKSPACE", -4: "TR_EHIP"}
 
@@ -101,6 +102,8 @@ def load_library():
     lib.moe_combine_epilogue.restype = st
     lib.moe_combine_epilogue.argtypes = [C.c_int64, C.c_int32, C.c_int64, C.c_int32, vp, vp,
                                          C.c_int64, vp, vp]
+    lib.moe_forward_noalloc.restype = st
+    lib.moe_forward_noalloc.argtypes = [C.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp]
     lib.moe_plan_stats.restype = st
     lib.moe_plan_stats.argtypes = [C.POINTER(PlanStruct), C.POINTER(C.c_int32), vp]
     lib.moe_last_error.restype = C.c_char_p
@@ -275,6 +278,35 @@ def forward(p: MoePlan, x: torch.Tensor, topk_weights: Optional[torch.Tensor],
                                       C.c_void_p(wp), C.c_void_p(w1p or None),
                                       C.c_void_p(w2p or None), C.c_void_p(yp or None),
                                       _stream_ptr(stream, p.ws.device)))
+    return y
+
+
+def forward_noalloc(topk_idx: torch.Tensor, x: torch.Tensor, topk_weights: Optional[torch.Tensor],
+                    w1: torch.Tensor, w2: torch.Tensor, y: torch.Tensor, E: int,
+                    expert_begin: int = 0, flags: int = 0, stream=None) -> torch.Tensor:
+    """moe_forward_noalloc: plan + forward in the library's static workspace
+    (no workspace argument; y must be given, since this call is for callers
+    that allocate nothing)."""
+    if topk_idx.dim() != 2 or topk_idx.dtype not in (torch.int32, torch.int64):
+        raise TypeError("topk_idx must be an int32 or int64 [T, K] tensor")
+    T, K = topk_idx.shape
+    if w1.dim() != 3:
+        raise ValueError("w1 must be [E, 2I, H]")
+    H, I = x.shape[1], w1.shape[1] // 2
+    dt = x.dtype
+    desc = make_desc(T, K, E, H, I, dt, topk_idx.dtype, expert_begin, flags)
+    ip = _dev_tensor(topk_idx, "topk_idx") if T > 0 else 0
+    xp = _dev_tensor(x, "x", dt, (T, H))
+    w1p = _dev_tensor(w1, "w1", dt, (E, 2 * I, H))
+    w2p = _dev_tensor(w2, "w2", dt, (E, H, I))
+    yp = _dev_tensor(y, "y", dt, (T, H))
+    wp = None if topk_weights is None else _dev_tensor(topk_weights, "topk_weights",
+                                                       torch.float32, (T, K))
+    _check(load_library().moe_forward_noalloc(C.byref(desc), C.c_void_p(ip or None),
+                                              C.c_void_p(xp or None), C.c_void_p(wp),
+                                              C.c_void_p(w1p or None), C.c_void_p(w2p or None),
+                                              C.c_void_p(yp or None),
+                                              _stream_ptr(stream, x.device)))
     return y
 
 

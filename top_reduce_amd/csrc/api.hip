@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "tr_internal.h"
 
@@ -396,6 +397,78 @@ tr_status moe_combine_epilogue(int64_t T, int32_t J, int64_t H, tr_dtype dtype,
   if (n_recv > 0 && (s = check_buf(recv, "recv", true)) != TR_OK) return s;
   return hip_status(tr::combine_epilogue(T, J, H, dtype == TR_BF16, src, recv, n_recv, y, stream),
                     "moe_combine_epilogue launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: plan + forward in a workspace the library holds
+// itself, for callers that cannot allocate device memory (code under HIP graph
+// capture, serving loops, harnesses that forbid allocation).
+// ---------------------------------------------------------------------------
+namespace {
+
+// The workspace of moe_forward_noalloc. Each device the library runs on holds
+// its own copy from module load until the process ends. In host code this
+// name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns for it (noalloc_scratch_ptr).
+static __device__ __align__(256) unsigned char scratch[TR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch array, looked up once per device
+// with that device current; NULL (and *err set) if the lookup fails.
+void* noalloc_scratch_ptr(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess) return nullptr;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+tr_status moe_forward_noalloc(const tr_moe_desc* desc, const void* topk_idx, const void* x,
+                              const float* topk_weights, const void* w1, const void* w2,
+                              void* y, hipStream_t stream) {
+  tr_status s = check_desc(desc);
+  if (s != TR_OK) return s;
+  tr_moe_desc d = *desc;
+  // bf16 gathers x inside GEMM1, so the expanded rows are never needed
+  if (d.dtype == TR_BF16 && tr::gemm_can_gather(d)) d.flags |= TR_FLAG_NO_XE;
+  const size_t need = layout(d).total;
+  if (need > static_cast<size_t>(TR_NOALLOC_SCRATCH_BYTES))
+    return fail(TR_EUNSUPPORTED,
+                "moe_forward_noalloc: this batch needs %zu bytes of workspace, the library's "
+                "static scratch holds %zu (use moe_plan + moe_forward with a caller workspace)",
+                need, static_cast<size_t>(TR_NOALLOC_SCRATCH_BYTES));
+  const bool any = d.T > 0;
+  if ((s = check_buf(x, "x", any)) != TR_OK) return s;
+  if ((s = check_buf(w1, "w1", any)) != TR_OK) return s;
+  if ((s = check_buf(w2, "w2", any)) != TR_OK) return s;
+  if ((s = check_buf(y, "y", any)) != TR_OK) return s;
+  if (topk_weights && !aligned(topk_weights, 4)) return fail(TR_EINVAL, "topk_weights misaligned");
+  hipError_t e = hipSuccess;
+  void* ws = noalloc_scratch_ptr(&e);
+  if (!ws) return hip_status(e, "moe_forward_noalloc: address of the static scratch");
+  tr_moe_plan p;
+  if ((s = plan_rows(&d, topk_idx, 0, nullptr, ws, need, stream, &p)) != TR_OK) return s;
+  return moe_forward(&p, x, topk_weights, w1, w2, y, stream);
 }
 
 tr_status moe_plan_stats(const tr_moe_plan* plan, int32_t* host_out, hipStream_t stream) {
