@@ -365,7 +365,8 @@ __device__ __forceinline__ TileInfo tile_info(const GemmArgs& a, const int* pre,
 // Operand sources of a tile for this wave. Every address is in bounds by
 // construction: the A buffers (Xe, h) carry BM spare rows past R_cap, so a
 // tile may read BM rows from any segment start (rows past the segment only
-// feed discarded outputs); a gathered A reads row 0 of x for those rows; and
+// feed discarded outputs); a gathered A gives those rows an offset past the
+// buffer, which the range check turns into zeros without an access; and
 // a tile's weight rows never pass the expert's 2I (or H) rows because I is a
 // multiple of BN / 2 and H of BN.
 template <bool kSwiglu, bool kGather>
@@ -396,8 +397,11 @@ __device__ __forceinline__ TileSrc<kGather> tile_src(const GemmArgs& a, const Ti
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) {
       const int lr = wave * 64 + j * 8 + (ln >> 3);
-      const int row = lr < t.rows_valid ? a.gather[t.row0 + lr] : 0;
-      s.d_voff[j] = (static_cast<uint32_t>(row) * Kd + (chunk ^ (j & 1)) * 8) * 2;
+      // a row past the segment gets an offset past the buffer (x is under
+      // 2 GiB): its DMA writes zeros, so the MFMAs on it toggle no data bits
+      s.d_voff[j] = lr < t.rows_valid
+                        ? (static_cast<uint32_t>(a.gather[t.row0 + lr]) * Kd + (chunk ^ (j & 1)) * 8) * 2
+                        : 0x80000000u;
     }
   } else {
     const uint32_t lr = wave * 64 + (ln >> 3);
@@ -450,12 +454,13 @@ __device__ __forceinline__ int early_down_tiles(int total_m, int NT1, int NT2, i
   return min((G - tail) * ratio, m_done * NT2);
 }
 
-// Tiles begin + slot, begin + slot + nslots, ... below end of one GEMM, for
-// this block. pre / cnt_s / off_s: the LDS tables of gemm_prologue.
-template <bool kSwiglu, bool kGather>
-__device__ __forceinline__ void gemm_tiles(const GemmArgs& a, int I, const int* pre,
-                                           const int* cnt_s, const int* off_s, int total_m,
-                                           int begin, int end, int slot, int nslots) {
+// The tile loop of gemm_tiles (below). pre / cnt_s / off_s: the LDS tables
+// of gemm_prologue. kFused (GEMM2 only): the reduce folded into the epilogue
+// for the rows the plan's row_dst names (a.dst non-NULL).
+template <bool kSwiglu, bool kGather, bool kFused>
+__device__ __forceinline__ void gemm_tiles_impl(const GemmArgs& a, int I, const int* pre,
+                                                const int* cnt_s, const int* off_s, int total_m,
+                                                int begin, int end, int slot, int nslots) {
   constexpr int kOutCols = kSwiglu ? BN / 2 : BN;   // output columns per tile
   const int NT = (a.Nc + kOutCols - 1) / kOutCols;
   const int tid = threadIdx.x;
@@ -518,7 +523,7 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& a, int I, const int* 
   // reduce folded into GEMM2 (rows of received rows with one local slot go to
   // y): the slots of this lane's four rows of the current tile. Loaded ahead
   // of the operand loads so that the first use waits for none of them.
-  const bool fused = !kSwiglu && a.dst != nullptr;
+  constexpr bool fused = kFused;
   int slot_c[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -601,6 +606,17 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& a, int I, const int* 
 
     bool after_stores = stores_in_flight;
     int kt = 0;
+    // Steady state: while every DMA and weight load of the two steps reads
+    // the current tile (k-tile kt + 4 < nk), the sources are fixed and the
+    // loop selects nothing between tiles; the last steps take the general
+    // form below.
+#pragma clang loop unroll(disable)
+    while (kt + 4 < nk) {
+      ring_step<0, kSwiglu, kStores>(f, g, r1, after_stores, s0, kt + 2, s0, kt + 3);
+      after_stores = false;
+      ring_step<1, kSwiglu, kStores>(f, g, r0, false, s0, kt + 3, s0, kt + 4);
+      kt += 2;
+    }
 #pragma clang loop unroll(disable)
     do {
       int dk, lk;
@@ -629,12 +645,21 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& a, int I, const int* 
     const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
         Cb + static_cast<int64_t>(t.row0) * a.Nc, 0, static_cast<int>(out_left), kBufferFlags);
     const int hi = lane >> 5;
-    // reduce folded into GEMM2: each lane's four rows' y row and weight
-    int yrow[4];
-    uint16_t* __restrict__ Yb = static_cast<uint16_t*>(a.y);
+    // reduce folded into GEMM2: each of this lane's four rows goes to its
+    // received row of y (one local slot) or to O; rows past the segment store
+    // nothing
+    uint16_t* drow[4];
+    bool to_y[4], rvalid[4];
     if (fused) {
+      uint16_t* __restrict__ Yb = static_cast<uint16_t*>(a.y);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yrow[i] = slot_c[i] >= 0 ? slot_c[i] / a.K : -1;
+      for (int i = 0; i < 4; ++i) {
+        const int lrow = wm * 128 + i * 32 + (lane & 31);
+        to_y[i] = slot_c[i] >= 0;
+        rvalid[i] = lrow < t.rows_valid;
+        drow[i] = to_y[i] ? Yb + static_cast<int64_t>(slot_c[i] / a.K) * a.Nc
+                          : Cb + static_cast<int64_t>(t.row0 + lrow) * a.Nc;
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -685,19 +710,15 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& a, int I, const int* 
             // rounded once (the +0 start of the reduce's sum decides the sign
             // of zero); the other rows go to O. One store either way, through
             // a per-lane address; rows past the segment store nothing.
-            const bool to_y = yrow[i] >= 0;
             u32x4 v = out;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const uint32_t yv =
                   pack_bf16x2_hw(__builtin_fmaf(ywt[i], __uint_as_float(out[e] << 16), 0.0f),
                                  __builtin_fmaf(ywt[i], __uint_as_float(out[e] & 0xffff0000u), 0.0f));
-              v[e] = to_y ? yv : out[e];
+              v[e] = to_y[i] ? yv : out[e];
             }
-            const int lrow = wm * 128 + i * 32 + (lane & 31);
-            uint16_t* dst = to_y ? Yb + static_cast<int64_t>(yrow[i]) * a.Nc + col
-                                 : Cb + static_cast<int64_t>(t.row0 + lrow) * a.Nc + col;
-            if (lrow < t.rows_valid) *reinterpret_cast<u32x4*>(dst) = v;
+            if (rvalid[i]) *reinterpret_cast<u32x4*>(drow[i] + col) = v;
           }
         }
         // one weight block at a time: the register stages stay live here
@@ -715,6 +736,26 @@ __device__ __forceinline__ void gemm_tiles(const GemmArgs& a, int I, const int* 
     s2 = src_of(L + 3 * G);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0, true));   // loads and DMA past the last tile
+}
+
+// Tiles begin + slot, begin + slot + nslots, ... below end of one GEMM, for
+// this block; GEMM2 with a.dst takes the fused epilogue (one branch per
+// launch, not per store).
+template <bool kSwiglu, bool kGather>
+__device__ __forceinline__ void gemm_tiles(const GemmArgs& a, int I, const int* pre,
+                                           const int* cnt_s, const int* off_s, int total_m,
+                                           int begin, int end, int slot, int nslots) {
+  if constexpr (kSwiglu) {
+    gemm_tiles_impl<true, kGather, false>(a, I, pre, cnt_s, off_s, total_m, begin, end, slot,
+                                          nslots);
+  } else {
+    if (a.dst != nullptr)
+      gemm_tiles_impl<false, kGather, true>(a, I, pre, cnt_s, off_s, total_m, begin, end, slot,
+                                            nslots);
+    else
+      gemm_tiles_impl<false, kGather, false>(a, I, pre, cnt_s, off_s, total_m, begin, end, slot,
+                                             nslots);
+  }
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
@@ -748,10 +789,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I, int pa
 //
 // y may alias x. Early GEMM2 tiles write y only for received rows with one
 // local slot, and that slot lies in an m-tile GEMM1 has already finished, so
-// no GEMM1 tile of this launch reads such a row as one of its own. A GEMM1
-// tile does read row 0 of x for the rows past its segment; if y[0] is being
-// written meanwhile, only those filler rows see it, and their outputs are
-// dropped by the store range check.
+// no GEMM1 tile of this launch reads such a row as one of its own; rows
+// past a segment are not read at all (their DMA offset lies past x).
 template <bool kGather>
 __global__ __launch_bounds__(kThreads) void gemm_hybrid(GemmArgs g1, GemmArgs g2, int I) {
 #if defined(__HIP_DEVICE_COMPILE__)
