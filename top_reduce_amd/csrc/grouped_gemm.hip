@@ -181,20 +181,20 @@ __device__ __forceinline__ u32x4* stage_b() { return S == 0 ? g_b0 : g_b1; }
 constexpr int kPieces = 8;
 
 // Where one tile's operands come from, for this wave and lane. Pieces are 8
-// rows apart: a lane keeps one byte offset for even and one for odd pieces
-// (the swizzle differs) and the pieces' row offsets go in the scalar offset.
-// Gathered activation rows are arbitrary, so there a lane keeps one offset per
-// activation piece.
+// rows apart. Weight pieces: a lane keeps one byte offset for even and one
+// for odd pieces (the swizzle differs) and the pieces' row offsets go in the
+// scalar offset. Activation pieces: a lane keeps one offset per piece, so that
+// a row past the segment can be given an offset past the buffer (the range
+// check covers the vector offset only), whose DMA writes zeros; gathered rows
+// are arbitrary anyway.
 template <bool kGather>
 struct TileSrc {
   __amdgpu_buffer_rsrc_t d_rsrc, r_rsrc;   // activations (DMA), weights (registers)
-  uint32_t d_voff[kGather ? kPieces : 2];  // this lane's activation offsets, k-tile 0
+  uint32_t d_voff[kPieces];  // this lane's activation offsets, k-tile 0
   uint32_t r_voff, r_voff1; // this lane's byte offset in weight piece 0 / 1, k-tile 0
   uint32_t stride;          // bytes between pieces j and j + 1 (8 rows)
-  __device__ __forceinline__ uint32_t a_voff(int j) const {
-    return kGather ? d_voff[j] : d_voff[j & 1];
-  }
-  __device__ __forceinline__ uint32_t a_soff(int j) const { return kGather ? 0u : j * stride; }
+  __device__ __forceinline__ uint32_t a_voff(int j) const { return d_voff[j]; }
+  __device__ __forceinline__ uint32_t a_soff(int) const { return 0u; }
 };
 
 struct TileInfo {
@@ -378,8 +378,12 @@ __device__ __forceinline__ TileSrc<kGather> tile_src(const GemmArgs& a, const Ti
   const uint16_t* abase = static_cast<const uint16_t*>(a.A);
   uint64_t left = static_cast<uint64_t>(a.a_rows) * Kd * 2;
   if (!kGather) {
+    // the tile's rows only: at most BM * Kd * 2 <= 2^31 bytes, so an offset
+    // of 2^31 is past the buffer
     abase += static_cast<int64_t>(t.row0) * Kd;
     left -= static_cast<uint64_t>(t.row0) * Kd * 2;
+    const uint64_t tile_bytes = static_cast<uint64_t>(BM) * Kd * 2;
+    left = left < tile_bytes ? left : tile_bytes;
   }
   s.d_rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(abase), 0,
                                                static_cast<int>(left < 0xffffffffull ? left : 0xffffffffull),
@@ -404,9 +408,13 @@ __device__ __forceinline__ TileSrc<kGather> tile_src(const GemmArgs& a, const Ti
                         : 0x80000000u;
     }
   } else {
-    const uint32_t lr = wave * 64 + (ln >> 3);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) s.d_voff[j] = (lr * Kd + (chunk ^ j) * 8) * 2;
+    for (int j = 0; j < kPieces; ++j) {
+      const int lr = wave * 64 + j * 8 + (ln >> 3);
+      s.d_voff[j] = lr < t.rows_valid
+                        ? (static_cast<uint32_t>(lr) * Kd + (chunk ^ (j & 1)) * 8) * 2
+                        : 0x80000000u;
+    }
   }
   int b_row;
   if (kSwiglu) b_row = wave < 2 ? t.n0 + wave * 64 : I + t.n0 + (wave - 2) * 64;  // gate | up
