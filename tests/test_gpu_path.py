@@ -21,6 +21,9 @@ pytestmark = pytest.mark.gpu
 gen.custom_spec("mid", T=1024, K=8, E=8, G=64, H=1024, I=512, zipf_s=1.0, seed=7)
 gen.custom_spec("mid_small_experts", T=512, K=4, E=32, G=128, H=512, I=256, zipf_s=0.6, seed=8)
 gen.custom_spec("mid_f32", T=300, K=4, E=6, G=12, H=264, I=72, dtype="f32", zipf_s=0.5, seed=9)
+# fp32 with I not a multiple of 4 (ragged k tail of GEMM2, ragged output
+# columns of GEMM1) and H not a multiple of 16
+gen.custom_spec("odd_f32", T=200, K=3, E=5, G=9, H=136, I=70, dtype="f32", zipf_s=0.5, seed=12)
 # every row routes to all 8 experts: 8 segments of 2080 rows, 9 m-tiles each
 # (the last one 32 rows deep); 288 tiles per GEMM, more than one round of the
 # persistent grid on 256 compute units.
@@ -46,7 +49,8 @@ def _forward(wl, flags=0, y_alias=False, weights=True):
     return p, host(y)
 
 
-@pytest.mark.parametrize("name,flags", [("c1", 0), ("mid_f32", 0), ("mid", 0), ("rounds", 0),
+@pytest.mark.parametrize("name,flags", [("c1", 0), ("mid_f32", 0), ("odd_f32", 0), ("mid", 0),
+                                        ("rounds", 0),
                                         ("mid", tr.FLAG_GEMM_FORCE_TILED),
                                         ("mid", tr.FLAG_GEMM_FORCE_STREAM),
                                         ("mid_small_experts", 0)])

@@ -30,7 +30,8 @@
 //    up to 32 token rows ride in the B operand; the reduction dimension is
 //    split over the four waves of a block and summed in LDS in a fixed order.
 //
-// An fp32 variant (gemm_f32) covers fp32 inputs with plain fp32 FMAs.
+// An fp32 variant (gemm_f32) covers fp32 inputs on fp32 MFMA
+// (v_mfma_f32_16x16x4_f32), one wave per 16 x 16 output tile.
 #include "tr_device.h"
 #include "tr_internal.h"
 
@@ -958,77 +959,93 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
 }
 
 // --------------------------------------------------------------------------
-// fp32 kernel: 32 rows x 32 outputs per tile, plain FMAs in k order
+// fp32 kernel: fp32 MFMA (v_mfma_f32_16x16x4_f32), one wave per 16-row x
+// 16-output tile
 // --------------------------------------------------------------------------
-constexpr int F_BM = 32, F_BN = 32, F_BK = 32;
+// A 16x16x4 MFMA takes from lane l the A element (row l % 16, k l / 16) and
+// the B element (k l / 16, column l % 16), and leaves in lane l the outputs
+// (rows 4 (l / 16) + 0..3, column l % 16). Here lane l loads four consecutive
+// k of its row, k0 + 4 (l / 16) + 0..3, from the activation row and from the
+// weight row(s); MFMA step s uses element s, so the four steps of a 16-k
+// chunk cover k0 .. k0 + 15 once each. Activation rows past the segment,
+// weight rows past the last output column and k past the end load as zero (no
+// access); outputs are stored only for valid rows and columns. fp32 shapes are
+// small (the tiny fp32 workload), so tiles are small for parallelism and
+// operands come straight from global memory, four chunks of loads ahead of
+// their MFMAs.
+constexpr int F_BM = 16, F_BN = 16, F_BK = 16;
 
 template <bool kSwiglu>
 __global__ __launch_bounds__(kThreads) void gemm_f32(GemmArgs a, int I) {
   __shared__ int pre[kMaxE + 1];
   __shared__ int tmp[kThreads / kWave];
-  __shared__ float As[F_BM][F_BK + 1];
-  __shared__ float Bs[2 * F_BN][F_BK + 1];
 
   const int total_m = expert_prefix(a.counts, a.E, [](int c) {
     return c > 0 ? (c + F_BM - 1) / F_BM : 0;
   }, pre, tmp);
   const int NT = (a.Nc + F_BN - 1) / F_BN;
   const int total = total_m * NT;
-  const int tid = threadIdx.x;
-  const int ty = tid >> 4, tx = tid & 15;   // rows 2*ty+{0,1}, cols 2*tx+{0,1}
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
   const int Kd = a.Kd;
+  const bool vec = (Kd & 3) == 0;   // rows start 16-byte aligned: float4 loads
   const int64_t Nb = kSwiglu ? 2 * static_cast<int64_t>(I) : a.Nc;
-  const int nbrows = kSwiglu ? 2 * F_BN : F_BN;
   const float* __restrict__ Af = static_cast<const float*>(a.A);
   const float* __restrict__ Bf = static_cast<const float*>(a.B);
   float* __restrict__ Cf = static_cast<float*>(a.C);
 
-  for (int L = blockIdx.x; L < total; L += gridDim.x) {
+  // four floats of row p at k .. k + 3, zero past Kd (p == nullptr: zero)
+  auto load4 = [Kd, vec](const float* p, int k, float* v) {
+    if (p && vec && k < Kd) {
+      const floatx4 q = *reinterpret_cast<const floatx4*>(p + k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = q[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (p && k + i < Kd) ? p[k + i] : 0.0f;
+    }
+  };
+
+  for (int L = blockIdx.x * (kThreads / kWave) + wave; L < total;
+       L += gridDim.x * (kThreads / kWave)) {
     const int gm = L / NT, nt = L % NT;
     const int e = find_expert(pre, a.E, gm);
     const int mt = gm - pre[e];
     const int row0 = a.offsets[e] + mt * F_BM;
     const int rows_valid = min(F_BM, a.counts[e] - mt * F_BM);
-    const int n0 = nt * F_BN;
-    float accg[2][2] = {{0, 0}, {0, 0}}, accu[2][2] = {{0, 0}, {0, 0}};
-    for (int k0 = 0; k0 < Kd; k0 += F_BK) {
-      for (int i = tid; i < F_BM * F_BK; i += kThreads) {
-        const int r = i / F_BK, k = i % F_BK;
-        const int rr = min(r, rows_valid - 1);
-        As[r][k] = (k0 + k < Kd) ? Af[static_cast<int64_t>(row0 + rr) * Kd + k0 + k] : 0.0f;
+    const int col = nt * F_BN + lr;
+    const bool cv = col < a.Nc;
+    const float* we = Bf + static_cast<int64_t>(e) * Nb * Kd;
+    const float* ap = lr < rows_valid ? Af + static_cast<int64_t>(row0 + lr) * Kd : nullptr;
+    const float* gp = cv ? we + static_cast<int64_t>(col) * Kd : nullptr;
+    const float* up = (kSwiglu && cv) ? we + static_cast<int64_t>(I + col) * Kd : nullptr;
+    floatx4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+    constexpr int kChunks = 4;
+    for (int k0 = 0; k0 < Kd; k0 += kChunks * F_BK) {
+      float av[kChunks][4], gv[kChunks][4], uv[kChunks][4];
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const int k = k0 + c * F_BK + 4 * lq;
+        load4(ap, k, av[c]);
+        load4(gp, k, gv[c]);
+        if (kSwiglu) load4(up, k, uv[c]);
       }
-      for (int i = tid; i < nbrows * F_BK; i += kThreads) {
-        const int r = i / F_BK, k = i % F_BK;
-        int64_t brow;
-        if (kSwiglu) {
-          const int c = min(n0 + (r % F_BN), I - 1);
-          brow = r < F_BN ? c : I + c;
-        } else {
-          brow = min(n0 + r, a.Nc - 1);
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          accg = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c][st], gv[c][st], accg, 0, 0, 0);
+          if (kSwiglu) accu = __builtin_amdgcn_mfma_f32_16x16x4f32(av[c][st], uv[c][st], accu, 0, 0, 0);
         }
-        Bs[r][k] = (k0 + k < Kd) ? Bf[(static_cast<int64_t>(e) * Nb + brow) * Kd + k0 + k] : 0.0f;
-      }
-      __syncthreads();
-      for (int k = 0; k < F_BK; ++k) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            accg[i][j] = fmaf(As[2 * ty + i][k], Bs[2 * tx + j][k], accg[i][j]);
-            if (kSwiglu) accu[i][j] = fmaf(As[2 * ty + i][k], Bs[F_BN + 2 * tx + j][k], accu[i][j]);
-          }
-      }
-      __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int r = 2 * ty + i, col = n0 + 2 * tx + j;
-        if (r < rows_valid && col < a.Nc)
-          Cf[static_cast<int64_t>(row0 + r) * a.Nc + col] =
-              kSwiglu ? silu_mul(accg[i][j], accu[i][j]) : accg[i][j];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int r = 4 * lq + q;
+      if (r < rows_valid && cv)
+        Cf[static_cast<int64_t>(row0 + r) * a.Nc + col] =
+            kSwiglu ? silu_mul(accg[q], accu[q]) : accg[q];
+    }
   }
 }
 
@@ -1068,10 +1085,12 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   hipError_t err;
 
   if (d.dtype == TR_F32) {
+    // one tile per wave, four waves per block
     const int64_t tiles1 = (cdiv(p.R_cap, F_BM) + E) * cdiv(I, F_BN);
     const int64_t tiles2 = (cdiv(p.R_cap, F_BM) + E) * cdiv(d.H, F_BN);
-    const unsigned grid1 = static_cast<unsigned>(tiles1 < cus * 8 ? tiles1 : cus * 8);
-    const unsigned grid2 = static_cast<unsigned>(tiles2 < cus * 8 ? tiles2 : cus * 8);
+    const int64_t b1 = cdiv(tiles1, kThreads / kWave), b2 = cdiv(tiles2, kThreads / kWave);
+    const unsigned grid1 = static_cast<unsigned>(b1 < cus * 8 ? b1 : cus * 8);
+    const unsigned grid2 = static_cast<unsigned>(b2 < cus * 8 ? b2 : cus * 8);
     if (up) {
       hipLaunchKernelGGL(gemm_f32<true>, dim3(grid1), dim3(kThreads), 0, st, g1, I);
       if ((err = hipGetLastError()) != hipSuccess) return err;
