@@ -31,6 +31,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
+// A block keeps each of its slots' local expert and expanded row in LDS for
+// the last phase when it has at most this many slots (else it re-reads them).
+constexpr int kSlotCache = 2048;
 
 template <typename IdxT>
 __device__ __forceinline__ int local_of(IdxT id, int64_t eb, int E) {
@@ -67,8 +70,10 @@ __device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1,
     const int64_t r = base + threadIdx.x;
     const bool in = r < r1 && (B == 0 || carries(r, B, bc));
     bool any = false;
-    if (in)
+    if (in) {
+#pragma unroll 8
       for (int k = 0; k < K; ++k) any |= local_of(idx[r * K + k], eb, E) < E;
+    }
     const uint64_t m = __ballot(any);
     if (lane_id() == 0 && m) atomicAdd(&cnt[E + 1], __popcll(m));
     const uint64_t c = __ballot(in);
@@ -108,6 +113,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   int* cnt = wcnt + kWaves * (E + 1);   // [E + 3] own counts (kSelf)
   int* tmp = cnt + (E + 3);             // [kWaves] scan scratch
   int* misc = tmp + kWaves;             // [4]
+  int* slot_e = misc + 4;               // [kSlotCache] local expert of each slot (E: none)
+  int* slot_row = slot_e + kSlotCache;  // [kSlotCache] its expanded row (-1: none)
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -119,12 +126,51 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   for (int i = tid; i < E; i += kThreads) prior[i] = 0;
   if (tid < 4) misc[tid] = 0;
   if (kSelf && tid == 0) stats[4] = 0;   // tok_rest entries (phase 3)
+  const int64_t s0 = r0 * K, s1 = r1 * K;
+  const bool cache = s1 - s0 <= kSlotCache;
+  // the local expert of each of this block's slots (E: none), loaded before
+  // phase 1's loads so that both wait for memory once; kept in LDS for the
+  // ranking and the last phase
+  constexpr int kPer = kSlotCache / kThreads;
+  int pe[kPer];
+  if (cache) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int64_t s = s0 + tid + u * kThreads;
+      pe[u] = (s < s1 && (B == 0 || carries(s / K, B, bc))) ? local_of(idx[s], eb, E) : E;
+    }
+  }
   __syncthreads();
   if (kSelf) {
     count_rows(idx, r0, r1, K, eb, E, B, bc, cnt);
+  } else if (E <= kThreads) {
+    // totals and this block's prior counts from every block's partials:
+    // thread tid sums expert tid % E over the blocks tid / E, + kThreads / E,
+    // ... in registers (independent loads, 16 in flight), then one LDS add
+    const int e = tid % E, lanes = kThreads / E, b0 = tid / E;
+    int all = 0, before = 0;
+    if (b0 < lanes) {
+      int b = b0;
+      for (; b + 15 * lanes < nblocks; b += 16 * lanes) {
+        int c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) c[u] = hist[(b + u * lanes) * (E + 3) + e];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          all += c[u];
+          if (b + u * lanes < static_cast<int>(blockIdx.x)) before += c[u];
+        }
+      }
+      for (; b < nblocks; b += lanes) {
+        const int c = hist[b * (E + 3) + e];
+        all += c;
+        if (b < static_cast<int>(blockIdx.x)) before += c;
+      }
+      if (all) atomicAdd(&cnt[e], all);
+      if (before) atomicAdd(&prior[e], before);
+    }
   } else {
-    // totals and this block's prior counts from every block's partials; all
-    // threads share the (block, expert) grid so the loads are independent
+    // many experts: all threads share the (block, expert) grid
     const int n = nblocks * E;
     for (int i = tid; i < n; i += kThreads) {
       const int b = i / E, e = i - b * E;
@@ -133,6 +179,13 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
         atomicAdd(&cnt[e], c);
         if (b < static_cast<int>(blockIdx.x)) atomicAdd(&prior[e], c);
       }
+    }
+  }
+  if (cache) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int64_t s = s0 + tid + u * kThreads;
+      if (s < s1) slot_e[s - s0] = pe[u];
     }
   }
   __syncthreads();
@@ -199,11 +252,12 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
 
   // 2. stable ranks, one round of kThreads slots at a time.
   const int nbits = 32 - __clz(E);  // bits of the values 0..E
-  const int64_t s0 = r0 * K, s1 = r1 * K;
   for (int64_t rb = s0; rb < s1; rb += kThreads) {
     const int64_t s = rb + tid;
     const bool in = s < s1;
-    const int e = in && (B == 0 || carries(s / K, B, bc)) ? local_of(idx[s], eb, E) : E;
+    const int e = !in ? E
+                  : cache ? slot_e[s - s0]
+                  : (B == 0 || carries(s / K, B, bc)) ? local_of(idx[s], eb, E) : E;
     const bool valid = e < E;
     uint64_t peers = __ballot(1);
     for (int b = 0; b < nbits; ++b) {
@@ -233,6 +287,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
         row_src[row] = static_cast<int>(s / K);
         row_k[row] = static_cast<int>(s % K);
       }
+      if (cache) slot_row[s - s0] = row;
     }
   }
 
@@ -248,15 +303,30 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     const int64_t t = tb + tid;
     bool rest = false;
     if (t < r1) {
-      int n = 0, k1 = 0;
-      for (int k = 0; k < K; ++k)
-        if (row_map[t * K + k] >= 0) {
+      // this block's slots: from LDS, or from row_map and idx if too many
+      auto slot_of = [&](int k, int* e_out) {
+        const int64_t s = t * K + k;
+        if (cache) {
+          *e_out = slot_e[s - s0];
+          return slot_row[s - s0];
+        }
+        const int m = row_map[s];
+        *e_out = m >= 0 ? local_of(idx[s], eb, E) : E;
+        return m;
+      };
+      int n = 0, k1 = 0, e1 = E;
+      for (int k = 0; k < K; ++k) {
+        int ek;
+        if (slot_of(k, &ek) >= 0) {
           ++n;
           k1 = k;
+          e1 = ek;
         }
-      const bool direct = n == 1 && cnt[local_of(idx[t * K + k1], eb, E)] >= min_tiled;
+      }
+      const bool direct = n == 1 && cnt[e1] >= min_tiled;
       for (int k = 0; k < K; ++k) {
-        const int m = row_map[t * K + k];
+        int ek;
+        const int m = slot_of(k, &ek);
         if (m >= 0) row_dst[m] = direct ? static_cast<int>(t * K + k) : -1;
       }
       rest = !direct;
@@ -274,7 +344,8 @@ hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
   const tr_moe_desc& d = p.d;
   const int E = d.E, K = d.K;
   const int nb = p.scan_blocks, rpb = p.scan_rows_per_block;
-  const size_t sh_scatter = sizeof(int) * (2 * E + kWaves * (E + 1) + (E + 3) + kWaves + 4);
+  const size_t sh_scatter =
+      sizeof(int) * (2 * E + kWaves * (E + 1) + (E + 3) + kWaves + 4 + 2 * kSlotCache);
   const int B = p.block_rows;
   const int* bc = p.block_counts;
   // fewest routes of an expert the grouped GEMM tiles (the others stream)
@@ -305,14 +376,15 @@ hipError_t route_scan(const tr_moe_plan& p, const void* idx, hipStream_t st) {
 }
 
 void route_scan_geometry(int64_t T, int K, int* blocks, int* rows_per_block) {
-  // One block for small inputs; otherwise ~1024 slots per block, at most
+  // One block for small inputs; otherwise ~512 slots per block (two ranking
+  // rounds: the blocks are latency-bound, so more and shorter ones), at most
   // kMaxScanBlocks blocks.
   if (T * K <= 4096) {
     *blocks = 1;
     *rows_per_block = static_cast<int>(T > 0 ? T : 1);
     return;
   }
-  int64_t rpb = cdiv(1024, K);
+  int64_t rpb = cdiv(512, K);
   if (cdiv(T, rpb) > kMaxScanBlocks) rpb = cdiv(T, kMaxScanBlocks);
   *rows_per_block = static_cast<int>(rpb);
   *blocks = static_cast<int>(cdiv(T, rpb));
