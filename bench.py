@@ -702,7 +702,10 @@ def main():
         roofline = {"bound": "mfma", "achieved": ach, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
                     "frac": ach / PEAK_F32_TFLOPS}
     roofline = {"kernel": "grouped GEMM, both projections, as moe_forward launches them",
-                **roofline, "traffic": stored_traffic("gemm_forward", args.config, "grouped_gemm.hip"),
+                **roofline,
+                "traffic": stored_traffic("gemm_forward",
+                                          args.config + (f"_T{args.T}" if args.T else ""),
+                                          "grouped_gemm.hip"),
                 "us_per_step": gemm_fwd_us, "algorithmic_flops": both_flops,
                 "algorithmic_bytes": both_bytes, "launches": launches,
                 "method": "HIP events around moe_forward in eager steps, minus the reduce"
