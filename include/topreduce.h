@@ -177,7 +177,8 @@ tr_status moe_plan_padded(const tr_moe_desc* desc, const void* topk_idx, int32_t
  * carrying rows. src: device [T or compact rows, row_bytes]; dst likewise;
  * no overlap. row_bytes a positive multiple of 4 with src and dst 4-byte
  * aligned (16-byte copies when row_bytes and both pointers allow); at most
- * 4096 blocks; T == 0 writes only n_out. Bit copies: works for x, topk_idx
+ * 4096 blocks and T < 2^31 (else TR_EUNSUPPORTED); T == 0 writes only n_out.
+ * Bit copies: works for x, topk_idx
  * and topk_weights alike. */
 tr_status moe_compact_rows(int64_t T, int32_t block_rows, const int32_t* block_counts,
                            int64_t row_bytes, const void* src, void* dst, int32_t to_padded,

@@ -210,6 +210,8 @@ tr_status moe_compact_rows(int64_t T, int32_t block_rows, const int32_t* block_c
                            int64_t row_bytes, const void* src, void* dst, int32_t to_padded,
                            int32_t* n_out, hipStream_t stream) {
   if (T < 0) return fail(TR_EINVAL, "T must be >= 0");
+  // compact positions and row indices are 32-bit on the device
+  if (T >= (int64_t{1} << 31)) return fail(TR_EUNSUPPORTED, "T must be < 2^31 (got %lld)", (long long)T);
   if (block_rows < 1) return fail(TR_EINVAL, "block_rows must be >= 1 (got %d)", block_rows);
   if ((T + block_rows - 1) / block_rows > tr::kMaxPadBlocks)
     return fail(TR_EUNSUPPORTED, "at most %d padding blocks (T / block_rows)", tr::kMaxPadBlocks);
