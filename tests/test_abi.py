@@ -237,6 +237,7 @@ def test_combine_epilogue_checks_arguments_on_the_host():
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "_HERE", str(tmp_path))
+    monkeypatch.delenv("TOP_REDUCE_LIB", raising=False)
     with pytest.raises(ImportError):
         B.load_library()
 

@@ -57,7 +57,9 @@ _lib = None
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """The in-tree library, or the build named by TOP_REDUCE_LIB (the
+    host-sanitizer build of the same sources, for CPU checks)."""
+    return os.environ.get("TOP_REDUCE_LIB") or os.path.join(_HERE, _LIB_NAME)
 
 
 def load_library():
