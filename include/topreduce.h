@@ -124,7 +124,7 @@ typedef struct tr_moe_plan {
                               received row t has exactly one local slot and its
                               expert is one the tiled GEMM takes (see
                               moe_grouped_gemm_down_y), else -1 */
-    int32_t* tok_rest;     /* [T] the other received rows, in no particular order;
+    int32_t* tok_rest;     /* [T] the other received rows, in ascending order;
                               stats[4] of them */
     int32_t block_rows;    /* moe_plan_padded: rows per worker block; 0 otherwise */
     int32_t reserved2;

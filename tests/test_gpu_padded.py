@@ -50,7 +50,9 @@ def _check_route(idx_np, E, B, counts, idx_dtype=torch.int64, flags=0):
     assert int(v["stats"][5]) == int(carry.sum())
     # padding rows are among the rows the reduce writes (as +0)
     n_rest = int(v["stats"][4])
-    rest = set(v["tok_rest"][:n_rest].cpu().numpy().tolist())
+    rest_rows = v["tok_rest"][:n_rest].cpu().numpy()
+    assert np.all(np.diff(rest_rows) > 0)   # ascending row order
+    rest = set(rest_rows.tolist())
     assert set(np.nonzero(~carry)[0].tolist()) <= rest
     return p
 

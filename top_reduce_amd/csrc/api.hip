@@ -86,7 +86,7 @@ Layout layout(const tr_moe_desc& d) {
   L.row_k = take(sizeof(int32_t) * L.R_cap);
   L.row_dst = take(sizeof(int32_t) * L.R_cap);
   L.tok_rest = take(sizeof(int32_t) * d.T);
-  L.scan_tmp = take(sizeof(int32_t) * static_cast<size_t>(L.blocks) * (d.E + 3));
+  L.scan_tmp = take(sizeof(int32_t) * static_cast<size_t>(L.blocks) * (2 * d.E + 4));
   L.Xe = take((d.flags & TR_FLAG_NO_XE) ? 0 : es * (L.R_cap + tr::kRowPad) * d.H);
   L.h = take(es * (L.R_cap + tr::kRowPad) * d.I);
   L.O = take(es * L.R_cap * d.H);

@@ -18,6 +18,11 @@
 //    expert id bit by bit, their rank is a popcount of the lower peers, and
 //    waves are chained in LDS. Positions never depend on atomic order, so the
 //    maps are bit-exact and deterministic.
+//  - the received rows that the fused GEMM2 epilogue does not complete
+//    (tok_rest) are listed in row order: `route_count` also counts, per block,
+//    the rows without exactly one local slot and, per expert, the rows whose
+//    one local slot goes to it, so each block's first entry follows from the
+//    same partial sums once the experts' totals are known.
 //  - a small input (T*K <= 4096) runs as one block that counts for itself:
 //    one launch instead of two.
 //  - a DP-padded buffer (SGLang PR #6092: workers' batches padded to one
@@ -50,10 +55,16 @@ __device__ __forceinline__ bool carries(int64_t r, int B, const int* __restrict_
   return r - j * B < bc[j];
 }
 
-// Adds the slots of rows [r0, r1) to cnt[0..E+3): per-expert counts, then
-// cnt[E] = ignored slots, cnt[E+1] = rows with at least one local slot,
-// cnt[E+2] = rows that carry a token. Rows that do not carry one count in
-// none of them.
+// Per-block counts, kept in LDS and in each block's row of `hist`
+// (hist_width(E) ints): [0, E) slots per local expert; then ignored slots,
+// rows with at least one local slot, rows that carry a token, rows whose
+// number of local slots is not one (rows that carry no token included); then
+// [E + 4, 2 E + 4) rows whose only local slot goes to expert e.
+__host__ __device__ constexpr int hist_width(int E) { return 2 * E + 4; }
+enum { kIgn = 0, kLocalRows = 1, kCarry = 2, kNotOne = 3 };   // offsets past E
+
+// Adds the slots and rows of rows [r0, r1) to cnt[0..hist_width(E)). Rows
+// that do not carry a token count as rows without one local slot only.
 template <typename IdxT>
 __device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1, int K,
                            int64_t eb, int E, int B, const int* __restrict__ bc, int* cnt) {
@@ -64,20 +75,29 @@ __device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1,
     const int e = in ? local_of(idx[s], eb, E) : E;
     if (e < E) atomicAdd(&cnt[e], 1);
     const uint64_t ign = __ballot(in && e == E);
-    if (lane_id() == 0 && ign) atomicAdd(&cnt[E], __popcll(ign));
+    if (lane_id() == 0 && ign) atomicAdd(&cnt[E + kIgn], __popcll(ign));
   }
   for (int64_t base = r0; base < r1; base += kThreads) {
     const int64_t r = base + threadIdx.x;
     const bool in = r < r1 && (B == 0 || carries(r, B, bc));
-    bool any = false;
+    int n = 0, e1 = E;
     if (in) {
 #pragma unroll 8
-      for (int k = 0; k < K; ++k) any |= local_of(idx[r * K + k], eb, E) < E;
+      for (int k = 0; k < K; ++k) {
+        const int e = local_of(idx[r * K + k], eb, E);
+        if (e < E) {
+          ++n;
+          e1 = e;
+        }
+      }
     }
-    const uint64_t m = __ballot(any);
-    if (lane_id() == 0 && m) atomicAdd(&cnt[E + 1], __popcll(m));
+    const uint64_t m = __ballot(n > 0);
+    if (lane_id() == 0 && m) atomicAdd(&cnt[E + kLocalRows], __popcll(m));
     const uint64_t c = __ballot(in);
-    if (lane_id() == 0 && c) atomicAdd(&cnt[E + 2], __popcll(c));
+    if (lane_id() == 0 && c) atomicAdd(&cnt[E + kCarry], __popcll(c));
+    const uint64_t no = __ballot(r < r1 && n != 1);
+    if (lane_id() == 0 && no) atomicAdd(&cnt[E + kNotOne], __popcll(no));
+    if (n == 1) atomicAdd(&cnt[E + 4 + e1], 1);
   }
 }
 
@@ -85,17 +105,23 @@ template <typename IdxT>
 __global__ __launch_bounds__(kThreads) void route_count(const IdxT* __restrict__ idx, int64_t T,
                                                         int K, int64_t eb, int E, int rpb, int B,
                                                         const int* __restrict__ bc,
-                                                        int* __restrict__ hist,
-                                                        int* __restrict__ stats) {
+                                                        int* __restrict__ hist) {
   extern __shared__ int cnt[];
-  if (blockIdx.x == 0 && threadIdx.x == 0) stats[4] = 0;   // tok_rest entries (route_scatter)
-  for (int i = threadIdx.x; i < E + 3; i += kThreads) cnt[i] = 0;
+  const int W = hist_width(E);
+  for (int i = threadIdx.x; i < W; i += kThreads) cnt[i] = 0;
   __syncthreads();
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rpb;
   const int64_t r1 = r0 + rpb < T ? r0 + rpb : T;
   count_rows(idx, r0, r1, K, eb, E, B, bc, cnt);
   __syncthreads();
-  for (int i = threadIdx.x; i < E + 3; i += kThreads) hist[blockIdx.x * (E + 3) + i] = cnt[i];
+  for (int i = threadIdx.x; i < W; i += kThreads) hist[blockIdx.x * W + i] = cnt[i];
+}
+
+// Sum of v over the wave (all lanes receive it).
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d);
+  return v;
 }
 
 // kSelf: single block, counts its own rows instead of reading `hist`.
@@ -107,14 +133,19 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     int* __restrict__ stats, int* __restrict__ row_dst, int* __restrict__ tok_rest,
     int min_tiled) {
   extern __shared__ int sh[];
+  const int W = hist_width(E);
   int* base = sh;                       // [E] first row of this block's slots per expert
   int* running = base + E;              // [E] rows taken so far by this block
   int* wcnt = running + E;              // [kWaves][E + 1] per-wave counts of a round
-  int* cnt = wcnt + kWaves * (E + 1);   // [E + 3] own counts (kSelf)
-  int* tmp = cnt + (E + 3);             // [kWaves] scan scratch
-  int* misc = tmp + kWaves;             // [4]
-  int* slot_e = misc + 4;               // [kSlotCache] local expert of each slot (E: none)
+  int* cnt = wcnt + kWaves * (E + 1);   // [W] totals over the blocks (own counts: kSelf)
+  int* tmp = cnt + W;                   // [kWaves] scan scratch
+  int* misc = tmp + kWaves;             // [8]
+  int* slot_e = misc + 8;               // [kSlotCache] local expert of each slot (E: none)
   int* slot_row = slot_e + kSlotCache;  // [kSlotCache] its expanded row (-1: none)
+  // misc: [0] empty experts, [1] ignored slots, [2] rows with a local slot,
+  // [3] carrying rows, [4] rows without one local slot in earlier blocks,
+  // [5] the same over all blocks, [6] / [7] rows whose one local slot goes
+  // to a streamed expert, in earlier blocks / in all blocks
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -122,63 +153,165 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   const int64_t r1 = r0 + rpb < T ? r0 + rpb : T;
 
   int* prior = wcnt;                    // [E] phase 1 only; wcnt is zeroed after
-  for (int i = tid; i < E + 3; i += kThreads) cnt[i] = 0;
-  for (int i = tid; i < E; i += kThreads) prior[i] = 0;
-  if (tid < 4) misc[tid] = 0;
-  if (kSelf && tid == 0) stats[4] = 0;   // tok_rest entries (phase 3)
+  int* sprior = wcnt + E;               // [E] likewise: one-slot rows in earlier blocks
+  for (int i = tid; i < W; i += kThreads) cnt[i] = 0;
+  for (int i = tid; i < 2 * E; i += kThreads) prior[i] = 0;
+  if (tid < 8) misc[tid] = 0;
   const int64_t s0 = r0 * K, s1 = r1 * K;
   const bool cache = s1 - s0 <= kSlotCache;
-  // the local expert of each of this block's slots (E: none), loaded before
-  // phase 1's loads so that both wait for memory once; kept in LDS for the
-  // ranking and the last phase
+  // The local expert of each of this block's slots (E: none), kept in LDS
+  // for the ranking and the last phase, and the other blocks' partial counts:
+  // all loaded before the first barrier, so that they wait for memory once.
+  // (The loads below are unconditional, with indices clamped into range and
+  // the extra values masked afterwards, so that they all go out before the
+  // first wait; a load under a per-lane condition would wait for its
+  // predecessors first. Padding rows' ids are the exception: never read.)
   constexpr int kPer = kSlotCache / kThreads;
   int pe[kPer];
+  IdxT pv[kPer] = {};   // raw ids (B == 0), converted once the other loads are out
+  if (cache) {
+    if (B == 0) {
+      // clamped to the block's last slot; an empty block (T == 0) loads none
+      if (s1 > s0) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int64_t s = s0 + tid + u * kThreads;
+          pv[u] = idx[s < s1 ? s : s1 - 1];
+        }
+      }
+    } else {
+      // padding rows' ids are not read: each id load has its own condition,
+      // and the ids are converted after the last load is out; the rows'
+      // block counts are read first, all at once (rows clamped to the
+      // block's last; an empty block (T == 0) reads none)
+      int bcv[kPer] = {};
+      if (s1 > s0) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int64_t s = s0 + tid + u * kThreads;
+          bcv[u] = bc[(s < s1 ? s : s1 - 1) / K / B];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        const int64_t s = s0 + tid + u * kThreads;
+        const int64_t r = s / K;
+        pe[u] = s < s1 && r - r / B * B < bcv[u] ? 1 : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < kPer; ++u)
+        if (pe[u]) pv[u] = idx[s0 + tid + u * kThreads];
+    }
+  }
+  // expert tid % E of blocks tid / E, + kThreads / E, ... (few enough experts
+  // that a thread holds all of its blocks' counts in registers)
+  constexpr int kHistPer = 32;
+  const int lanes = E <= kThreads ? kThreads / E : 1;
+  const bool hist_regs = !kSelf && E <= kThreads && cdiv(nblocks, lanes) <= kHistPer;
+  int hc[kHistPer], hs[kHistPer];
+  const int he = tid % E, hb0 = tid / E;
+  if (hist_regs) {
+    const int nper = static_cast<int>(cdiv(nblocks, lanes));   // uniform
+#pragma unroll
+    for (int u = 0; u < kHistPer; ++u) {
+      const int b = min(hb0 + u * lanes, nblocks - 1);
+      hc[u] = u < nper ? hist[b * W + he] : 0;
+      hs[u] = u < nper ? hist[b * W + E + 4 + he] : 0;
+    }
+  }
+  // block tid's row counts (nblocks <= kThreads)
+  int h_not1 = 0, h_ign = 0, h_loc = 0, h_car = 0;
+  if (!kSelf) {
+    const int b = min(tid, nblocks - 1);
+    h_not1 = hist[b * W + E + kNotOne];
+    h_ign = hist[b * W + E + kIgn];
+    h_loc = hist[b * W + E + kLocalRows];
+    h_car = hist[b * W + E + kCarry];
+    if (tid >= nblocks) h_not1 = h_ign = h_loc = h_car = 0;
+  }
   if (cache) {
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      const int64_t s = s0 + tid + u * kThreads;
-      pe[u] = (s < s1 && (B == 0 || carries(s / K, B, bc))) ? local_of(idx[s], eb, E) : E;
+      const bool has = B == 0 ? s0 + tid + u * kThreads < s1 : pe[u] != 0;
+      pe[u] = has ? local_of(pv[u], eb, E) : E;
     }
   }
   __syncthreads();
   if (kSelf) {
     count_rows(idx, r0, r1, K, eb, E, B, bc, cnt);
-  } else if (E <= kThreads) {
-    // totals and this block's prior counts from every block's partials:
-    // thread tid sums expert tid % E over the blocks tid / E, + kThreads / E,
-    // ... in registers (independent loads, 16 in flight), then one LDS add
-    const int e = tid % E, lanes = kThreads / E, b0 = tid / E;
-    int all = 0, before = 0;
-    if (b0 < lanes) {
-      int b = b0;
-      for (; b + 15 * lanes < nblocks; b += 16 * lanes) {
-        int c[16];
+  } else {
+    if (hist_regs) {
+      int all = 0, before = 0, sall = 0, sbefore = 0;
 #pragma unroll
-        for (int u = 0; u < 16; ++u) c[u] = hist[(b + u * lanes) * (E + 3) + e];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          all += c[u];
-          if (b + u * lanes < static_cast<int>(blockIdx.x)) before += c[u];
+      for (int u = 0; u < kHistPer; ++u) {
+        const int b = hb0 + u * lanes;
+        if (hb0 < lanes && b < nblocks) {
+          all += hc[u];
+          sall += hs[u];
+          if (b < static_cast<int>(blockIdx.x)) {
+            before += hc[u];
+            sbefore += hs[u];
+          }
         }
       }
-      for (; b < nblocks; b += lanes) {
-        const int c = hist[b * (E + 3) + e];
-        all += c;
-        if (b < static_cast<int>(blockIdx.x)) before += c;
+      if (all) atomicAdd(&cnt[he], all);
+      if (before) atomicAdd(&prior[he], before);
+      if (sall) atomicAdd(&cnt[E + 4 + he], sall);
+      if (sbefore) atomicAdd(&sprior[he], sbefore);
+    } else if (E <= kThreads) {
+      // more blocks per thread: the same sums, 16 loads in flight at a time
+      int all = 0, before = 0, sall = 0, sbefore = 0;
+      if (hb0 < lanes) {
+        for (int b = hb0; b < nblocks; b += 16 * lanes) {
+          int c[16], cs[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int bu = min(b + u * lanes, nblocks - 1);
+            c[u] = hist[bu * W + he];
+            cs[u] = hist[bu * W + E + 4 + he];
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const int bu = b + u * lanes;
+            if (bu < nblocks) {
+              all += c[u];
+              sall += cs[u];
+              if (bu < static_cast<int>(blockIdx.x)) {
+                before += c[u];
+                sbefore += cs[u];
+              }
+            }
+          }
+        }
       }
-      if (all) atomicAdd(&cnt[e], all);
-      if (before) atomicAdd(&prior[e], before);
+      if (all) atomicAdd(&cnt[he], all);
+      if (before) atomicAdd(&prior[he], before);
+      if (sall) atomicAdd(&cnt[E + 4 + he], sall);
+      if (sbefore) atomicAdd(&sprior[he], sbefore);
+    } else {
+      // many experts: all threads share the (block, expert) grid
+      const int n = nblocks * E;
+      for (int i = tid; i < n; i += kThreads) {
+        const int b = i / E, e = i - b * E;
+        const int c = hist[b * W + e], cs = hist[b * W + E + 4 + e];
+        if (c) atomicAdd(&cnt[e], c);
+        if (cs) atomicAdd(&cnt[E + 4 + e], cs);
+        if (b < static_cast<int>(blockIdx.x)) {
+          if (c) atomicAdd(&prior[e], c);
+          if (cs) atomicAdd(&sprior[e], cs);
+        }
+      }
     }
-  } else {
-    // many experts: all threads share the (block, expert) grid
-    const int n = nblocks * E;
-    for (int i = tid; i < n; i += kThreads) {
-      const int b = i / E, e = i - b * E;
-      const int c = hist[b * (E + 3) + e];
-      if (c) {
-        atomicAdd(&cnt[e], c);
-        if (b < static_cast<int>(blockIdx.x)) atomicAdd(&prior[e], c);
-      }
+    const int n1b = wave_sum(tid < static_cast<int>(blockIdx.x) ? h_not1 : 0);
+    const int n1a = wave_sum(h_not1);
+    // ignored slots, rows with a local slot and carrying rows: block 0's stats
+    const int ig = wave_sum(h_ign), lo = wave_sum(h_loc), ca = wave_sum(h_car);
+    if (lane_id() == 0) {
+      if (n1b) atomicAdd(&misc[4], n1b);
+      if (n1a) atomicAdd(&misc[5], n1a);
+      if (ig) atomicAdd(&misc[1], ig);
+      if (lo) atomicAdd(&misc[2], lo);
+      if (ca) atomicAdd(&misc[3], ca);
     }
   }
   if (cache) {
@@ -190,9 +323,11 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   }
   __syncthreads();
 
-  // 1. totals per expert, this block's prior count, segment offsets.
+  // 1. totals per expert, this block's prior count, segment offsets, and the
+  // tok_rest entries before this block's: rows without one local slot, and
+  // one-slot rows of streamed experts (fewer than min_tiled routes).
   const int per = (E + kThreads - 1) / kThreads;  // experts per thread (<= 4)
-  int tsum = 0;
+  int tsum = 0, rest_before = 0, rest_all = 0;
   int tot[4], pri[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -203,10 +338,20 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
       tot[j] = cnt[e];
       pri[j] = kSelf ? 0 : prior[e];
       tsum += tot[j];
+      if (tot[j] < min_tiled) {
+        rest_before += kSelf ? 0 : sprior[e];
+        rest_all += cnt[E + 4 + e];
+      }
     }
   }
+  rest_before = wave_sum(rest_before);
+  rest_all = wave_sum(rest_all);
   __syncthreads();                      // prior[] read; wcnt becomes per-wave counts
   for (int i = tid; i < kWaves * (E + 1); i += kThreads) wcnt[i] = 0;
+  if (lane_id() == 0) {
+    if (rest_before) atomicAdd(&misc[6], rest_before);
+    if (rest_all) atomicAdd(&misc[7], rest_all);
+  }
   int R = 0;
   int off = block_exclusive_scan<kThreads>(tsum, tmp, &R);
 #pragma unroll
@@ -223,32 +368,17 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
       off += tot[j];
     }
   }
-  if (blockIdx.x == 0) {
-    // ignored slots, rows with a local route and carrying rows, summed
-    // over blocks
-    if (kSelf) {
-      if (tid == 0) { misc[1] = cnt[E]; misc[2] = cnt[E + 1]; misc[3] = cnt[E + 2]; }
-    } else {
-      int ign = 0, tl = 0, cr = 0;
-      for (int b = tid; b < nblocks; b += kThreads) {
-        ign += hist[b * (E + 3) + E];
-        tl += hist[b * (E + 3) + E + 1];
-        cr += hist[b * (E + 3) + E + 2];
-      }
-      if (ign) atomicAdd(&misc[1], ign);
-      if (tl) atomicAdd(&misc[2], tl);
-      if (cr) atomicAdd(&misc[3], cr);
-    }
-  }
   __syncthreads();
   if (blockIdx.x == 0 && tid == 0) {
     offsets[E] = R;
     stats[0] = R;
-    stats[1] = misc[2];
-    stats[2] = misc[1];
+    stats[1] = kSelf ? cnt[E + kLocalRows] : misc[2];
+    stats[2] = kSelf ? cnt[E + kIgn] : misc[1];
     stats[3] = misc[0];
-    stats[5] = misc[3];
+    stats[4] = (kSelf ? cnt[E + kNotOne] : misc[5]) + misc[7];
+    stats[5] = kSelf ? cnt[E + kCarry] : misc[3];
   }
+  int rest_at = kSelf ? 0 : misc[4] + misc[6];
 
   // 2. stable ranks, one round of kThreads slots at a time.
   const int nbits = 32 - __clz(E);  // bits of the values 0..E
@@ -295,9 +425,9 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   // received row with exactly one local slot, whose expert has at least
   // min_tiled routes (the experts of the tiled kernel), names that slot;
   // other rows name none, and their received rows (and the ones with no
-  // local slot) join tok_rest. This block's rows are its own received rows,
-  // so its row_map entries are complete after the barrier; cnt[] holds the
-  // experts' totals.
+  // local slot) join tok_rest, in row order from this block's first entry.
+  // This block's rows are its own received rows, so its row_map entries are
+  // complete after the barrier; cnt[] holds the experts' totals.
   __syncthreads();
   for (int64_t tb = r0; tb < r1; tb += kThreads) {
     const int64_t t = tb + tid;
@@ -314,12 +444,11 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
         *e_out = m >= 0 ? local_of(idx[s], eb, E) : E;
         return m;
       };
-      int n = 0, k1 = 0, e1 = E;
+      int n = 0, e1 = E;
       for (int k = 0; k < K; ++k) {
         int ek;
         if (slot_of(k, &ek) >= 0) {
           ++n;
-          k1 = k;
           e1 = ek;
         }
       }
@@ -332,10 +461,16 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
       rest = !direct;
     }
     const uint64_t mask = __ballot(rest);
-    int at = 0;
-    if (lane_id() == 0 && mask) at = atomicAdd(&stats[4], __popcll(mask));
-    at = __shfl(at, 0);
-    if (rest) tok_rest[at + popc_below(mask)] = static_cast<int>(t);
+    if (lane_id() == 0) tmp[wave] = __popcll(mask);
+    __syncthreads();
+    int before = 0, chunk = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      if (w < wave) before += tmp[w];
+      chunk += tmp[w];
+    }
+    if (rest) tok_rest[rest_at + before + popc_below(mask)] = static_cast<int>(t);
+    rest_at += chunk;
+    __syncthreads();
   }
 }
 
@@ -345,21 +480,20 @@ hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
   const int E = d.E, K = d.K;
   const int nb = p.scan_blocks, rpb = p.scan_rows_per_block;
   const size_t sh_scatter =
-      sizeof(int) * (2 * E + kWaves * (E + 1) + (E + 3) + kWaves + 4 + 2 * kSlotCache);
+      sizeof(int) * (2 * E + kWaves * (E + 1) + hist_width(E) + kWaves + 8 + 2 * kSlotCache);
   const int B = p.block_rows;
   const int* bc = p.block_counts;
   // fewest routes of an expert the grouped GEMM tiles (the others stream)
   const int min_tiled = (d.flags & TR_FLAG_GEMM_FORCE_STREAM) ? INT32_MAX
                         : (d.flags & TR_FLAG_GEMM_FORCE_TILED) ? 1 : kStreamMaxRows + 1;
   if (nb == 1) {
-    // one block: its route_scatter zeroes the tok_rest count itself
     hipLaunchKernelGGL((route_scatter<IdxT, true>), dim3(1), dim3(kThreads), sh_scatter, st, idx,
                        d.T, K, d.expert_begin, E, rpb, nb, B, bc, p.scan_tmp, p.counts, p.offsets,
                        p.row_map, p.row_src, p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((route_count<IdxT>), dim3(nb), dim3(kThreads), sizeof(int) * (E + 3), st,
-                     idx, d.T, K, d.expert_begin, E, rpb, B, bc, p.scan_tmp, p.stats);
+  hipLaunchKernelGGL((route_count<IdxT>), dim3(nb), dim3(kThreads), sizeof(int) * hist_width(E),
+                     st, idx, d.T, K, d.expert_begin, E, rpb, B, bc, p.scan_tmp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((route_scatter<IdxT, false>), dim3(nb), dim3(kThreads), sh_scatter, st, idx,
