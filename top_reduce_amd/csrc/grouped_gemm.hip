@@ -922,35 +922,35 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
       red[wave][1][lane] = acc[1];
       __syncthreads();
       if (wave == 0) {
-        // output element (row 4*g + v, token lane & 15) of each token group
+        // lane (g, r) holds output columns 4 g .. 4 g + 3 of the unit (the
+        // weight rows) for token tb + 16 q + r; with the next four columns
+        // from lane + 16, lanes of even g store 8 columns with one 16-byte
+        // store (the unit's columns lie inside the row: I % 128 == 0,
+        // H % 256 == 0)
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int tok = tb + q * 16 + (lane & 15);
           floatx4 s = red[0][q][lane];
 #pragma unroll
           for (int w = 1; w < kThreads / kWave; ++w) s += red[w][q][lane];
+          uint32_t p0, p1;
           if (kSwiglu) {
+            // lanes 0..31 hold gate rows, lanes 32..63 the matching up rows
             floatx4 up = red[0][q][lane ^ 32];
 #pragma unroll
             for (int w = 1; w < kThreads / kWave; ++w) up += red[w][q][lane ^ 32];
-            if (lane < 32 && tok < cnt) {
-#pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                const int col = c * 8 + 4 * g + v;
-                if (col < I)
-                  Cb[static_cast<int64_t>(off + tok) * a.Nc + col] =
-                      static_cast<uint16_t>(f32_to_bf16_bits(silu_mul(s[v], up[v])));
-              }
-            }
-          } else if (tok < cnt) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const int col = c * 16 + 4 * g + v;
-              if (col < a.Nc)
-                Cb[static_cast<int64_t>(off + tok) * a.Nc + col] =
-                    static_cast<uint16_t>(f32_to_bf16_bits(s[v]));
-            }
+            p0 = pack_bf16x2(silu_mul(s[0], up[0]), silu_mul(s[1], up[1]));
+            p1 = pack_bf16x2(silu_mul(s[2], up[2]), silu_mul(s[3], up[3]));
+          } else {
+            p0 = pack_bf16x2(s[0], s[1]);
+            p1 = pack_bf16x2(s[2], s[3]);
           }
+          const uint32_t n0 = __shfl_down(p0, 16, kWave), n1 = __shfl_down(p1, 16, kWave);
+          const bool st = kSwiglu ? g == 0 : (g & 1) == 0;
+          const int col = kSwiglu ? c * 8 : c * 16 + 4 * g;
+          if (st && tok < cnt && col + 8 <= a.Nc)
+            *reinterpret_cast<u32x4*>(Cb + static_cast<int64_t>(off + tok) * a.Nc + col) =
+                u32x4{p0, p1, n0, n1};
         }
       }
       __syncthreads();
