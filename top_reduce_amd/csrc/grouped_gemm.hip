@@ -827,20 +827,77 @@ __global__ __launch_bounds__(kThreads) void gemm_hybrid(GemmArgs g1, GemmArgs g2
 // --------------------------------------------------------------------------
 constexpr int kStreamU = 8;  // k32 blocks per unrolled step
 
+// This wave's k32 blocks [kb0, kb1) of one token group: NQ groups of 16 rows
+// (the second only when the group has more than 16 rows, so that a decode
+// group issues no loads for it). MFMA j of a step takes k-block kb + j: lane
+// group g holds its 8 elements g * 8 .. g * 8 + 7, so one load instruction
+// reads 64 contiguous bytes of each of 16 rows (4 lanes per row).
+template <int NQ>
+__device__ __forceinline__ void stream_kloop(const uint16_t* __restrict__ wp,
+                                             const uint16_t* const (&xp)[2], const bool (&xv)[2],
+                                             int kb0, int kb1, int g, floatx4 (&acc)[2]) {
+  int kb = kb0;
+  for (; kb + kStreamU <= kb1; kb += kStreamU) {
+    const int k = kb * 32 + g * 8;
+    u32x4 wa[kStreamU], xb[NQ][kStreamU];
+#pragma unroll
+    for (int j = 0; j < kStreamU; ++j) wa[j] = *reinterpret_cast<const u32x4*>(wp + k + j * 32);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q)
+#pragma unroll
+      for (int j = 0; j < kStreamU; ++j)
+        xb[q][j] = xv[q] ? *reinterpret_cast<const u32x4*>(xp[q] + k + j * 32)
+                         : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < kStreamU; ++j)
+#pragma unroll
+      for (int q = 0; q < NQ; ++q)
+        acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, wa[j]), __builtin_bit_cast(bf16x8, xb[q][j]), acc[q],
+            0, 0, 0);
+  }
+  for (; kb < kb1; ++kb) {
+    const int k = kb * 32 + g * 8;
+    const u32x4 wa = *reinterpret_cast<const u32x4*>(wp + k);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const u32x4 xb = xv[q] ? *reinterpret_cast<const u32x4*>(xp[q] + k) : u32x4{0, 0, 0, 0};
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, wa), __builtin_bit_cast(bf16x8, xb), acc[q], 0, 0, 0);
+    }
+  }
+}
+
 template <bool kSwiglu>
 __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
   __shared__ int pre[kMaxE + 1];
   __shared__ int list[kMaxE];
+  __shared__ int cnt_s[kMaxE], off_s[kMaxE];
   __shared__ int tmp[kThreads / kWave];
   __shared__ floatx4 red[kThreads / kWave][2][kWave];
 
+  // the experts' segment offsets, loaded with the counts (one wait)
+  int offv[kMaxE / kThreads], cntv[kMaxE / kThreads];
+#pragma unroll
+  for (int j = 0; j < kMaxE / kThreads; ++j) {
+    const int e = threadIdx.x + j * kThreads;
+    offv[j] = e < a.E ? a.offsets[e] : 0;
+    cntv[j] = e < a.E ? a.counts[e] : 0;
+  }
   const int mode = a.mode;
   const int n_elig = expert_prefix(a.counts, a.E, [mode](int c) {
     return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
   }, pre, tmp);
   if (n_elig == 0) return;
-  for (int e = threadIdx.x; e < a.E; e += kThreads)
-    if (pre[e + 1] > pre[e]) list[pre[e]] = e;
+#pragma unroll
+  for (int j = 0; j < kMaxE / kThreads; ++j) {
+    const int e = threadIdx.x + j * kThreads;
+    if (e < a.E) {
+      if (pre[e + 1] > pre[e]) list[pre[e]] = e;
+      cnt_s[e] = cntv[j];
+      off_s[e] = offv[j];
+    }
+  }
   __syncthreads();
 
   const int cols = kSwiglu ? 8 : 16;               // outputs per unit
@@ -859,11 +916,28 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
   const uint16_t* __restrict__ Bb = static_cast<const uint16_t*>(a.B);
   uint16_t* __restrict__ Cb = static_cast<uint16_t*>(a.C);
 
+  // Gathered A: the ids of this lane's rows (q * 16 + arow) of unit u's first
+  // token group, loaded one unit ahead so that a unit starts with its rows
+  // known.
+  auto ids_of = [&](int u, int (&id)[2]) {
+    id[0] = id[1] = 0;
+    if (u >= total || !a.gather) return;
+    const int e = list[u / upe];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int t = q * 16 + arow;
+      if (t < cnt_s[e]) id[q] = a.gather[off_s[e] + t];
+    }
+  };
+  int id_next[2];
+  ids_of(blockIdx.x, id_next);
   for (int u = blockIdx.x; u < total; u += gridDim.x) {
     const int e = list[u / upe];
     const int c = u % upe;
-    const int cnt = a.counts[e];
-    const int off = a.offsets[e];
+    const int cnt = cnt_s[e];
+    const int off = off_s[e];
+    const int id0[2] = {id_next[0], id_next[1]};
+    ids_of(u + static_cast<int>(gridDim.x), id_next);
     int64_t wrow;
     if (kSwiglu) {
       const int col = min(c * 8 + (arow & 7), I - 1);
@@ -881,43 +955,13 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
         const int tok = tb + q * 16 + arow;
         xv[q] = tok < cnt;
         const int r = off + (xv[q] ? tok : 0);
-        xp[q] = Ab + static_cast<int64_t>(a.gather ? a.gather[r] : r) * Kd;
+        const int row = !a.gather ? r : tb == 0 ? id0[q] : a.gather[r];
+        xp[q] = Ab + static_cast<int64_t>(row) * Kd;
       }
 
       floatx4 acc[2] = {floatx4{0, 0, 0, 0}, floatx4{0, 0, 0, 0}};
-      int kb = kb0;
-      for (; kb + kStreamU <= kb1; kb += kStreamU) {
-        // MFMA j takes k-block kb + j: lane group g holds its 8 elements
-        // g * 8 .. g * 8 + 7, so one load instruction reads 64 contiguous
-        // bytes of each of 16 rows (4 lanes per row)
-        const int k = kb * 32 + g * 8;
-        u32x4 wa[kStreamU], xb[2][kStreamU];
-#pragma unroll
-        for (int j = 0; j < kStreamU; ++j) wa[j] = *reinterpret_cast<const u32x4*>(wp + k + j * 32);
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int j = 0; j < kStreamU; ++j)
-            xb[q][j] = xv[q] ? *reinterpret_cast<const u32x4*>(xp[q] + k + j * 32)
-                             : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < kStreamU; ++j)
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, wa[j]), __builtin_bit_cast(bf16x8, xb[q][j]), acc[q],
-                0, 0, 0);
-      }
-      for (; kb < kb1; ++kb) {
-        const int k = kb * 32 + g * 8;
-        const u32x4 wa = *reinterpret_cast<const u32x4*>(wp + k);
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const u32x4 xb = xv[q] ? *reinterpret_cast<const u32x4*>(xp[q] + k) : u32x4{0, 0, 0, 0};
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, wa), __builtin_bit_cast(bf16x8, xb), acc[q], 0, 0, 0);
-        }
-      }
+      if (cnt - tb > 16) stream_kloop<2>(wp, xp, xv, kb0, kb1, g, acc);
+      else stream_kloop<1>(wp, xp, xv, kb0, kb1, g, acc);
       red[wave][0][lane] = acc[0];
       red[wave][1][lane] = acc[1];
       __syncthreads();
