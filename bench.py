@@ -787,10 +787,28 @@ def main():
         cold["gemm_down"] = cold_us(lambda: tr.grouped_gemm_down_y(p, w2, w, y2, stream=stream))
         cold_bytes["gemm_up"] = gemm_bytes["gemm_up"]
         cold_bytes["gemm_down"] = gemm_bytes["gemm_down"]
+        if 0 < n_active <= 4:
+            # The vendor library on the same decode shape: one row against each
+            # active expert's W1 and W2 (torch.nn.functional.linear, a GEMV in
+            # rocBLAS / hipBLASLt), cold, timed like the GEMMs. Calibration
+            # only; nothing of the path runs here.
+            act = [int(e) for e in np.nonzero(p.views()["counts"].cpu().numpy())[0]]
+            xr = x[:1].contiguous()
+            hr = torch.ones((1, I), dtype=x.dtype, device=dev)
+            F = torch.nn.functional
+            cold["library_gemv_up"] = cold_us(lambda: [F.linear(xr, w1[e]) for e in act])
+            cold["library_gemv_down"] = cold_us(lambda: [F.linear(hr, w2[e]) for e in act])
+            cold_bytes["library_gemv_up"] = len(act) * 2 * I * H * b
+            cold_bytes["library_gemv_down"] = len(act) * H * I * b
     result["cold"] = {k: {"us": v, "achieved": cold_bytes[k] / v / 1e3, "unit": "GB/s",
                           "peak": PEAK_HBM_GBS, "frac": cold_bytes[k] / v / 1e3 / PEAK_HBM_GBS,
                           "method": "median of 10 launches, each after reading 1 GiB"}
                       for k, v in cold.items()}
+    for k in ("library_gemv_up", "library_gemv_down"):
+        if k in result["cold"]:
+            result["cold"][k]["kernel"] = ("torch.nn.functional.linear of one row against each "
+                                           "active expert's " + ("W1" if k.endswith("up") else "W2") +
+                                           " (vendor GEMV on the same weights; calibration)")
     for k in ("gemm_up", "gemm_down"):
         if k in result["cold"]:
             flops = work[k][1]
