@@ -94,6 +94,9 @@ def test_padded_route_edge_cases():
     _check_route(rng.integers(-1, 32, size=(T, 2)), 32, 1, rng.integers(0, 2, size=T))
     # T = 0
     _check_route(np.zeros((0, 8), np.int64), 4, 10, np.zeros(0, np.int32))
+    # 64 experts over ~254 scan blocks (batched partial sums)
+    T, B = 20000, 96
+    _check_route(rng.integers(-1, 64, size=(T, 8)), 64, B, rng.integers(0, B + 1, size=-(-T // B)))
 
 
 @pytest.fixture(scope="module")

@@ -76,6 +76,11 @@ def test_route_edge_cases():
     _check(rng.integers(-1, 1024, size=(4099, 32)), 1024)          # max E and K, ragged blocks
     _check(rng.integers(-1, 3, size=(70000, 3)), 3)                # many blocks, few experts
     _check(rng.integers(0, 8, size=(513, 8)), 8, idx_dtype=torch.int32)
+    # the partial sums of 32 < E <= 256 experts over ~254 blocks (batched
+    # loads per thread) and of blocks with more slots than the LDS slot cache
+    _check(rng.integers(-1, 64, size=(20000, 8)), 64)
+    _check(rng.integers(-1, 256, size=(30000, 8)), 256)
+    _check(rng.integers(-1, 48, size=(40000, 32)), 48)
 
 
 def test_route_deterministic():
