@@ -33,8 +33,14 @@ __global__ __launch_bounds__(kThreads) void compact_rows(int64_t T, int B, int n
   __shared__ int pre[kMaxPadBlocks + 1];   // block j: compact position of its first row
   __shared__ int tmp[kThreads / kWave];
   const int tid = threadIdx.x;
-  // clamped counts, kPerThread consecutive blocks per thread, then the scan
+  // clamped counts, kPerThread consecutive blocks per thread, then the scan.
+  // The loads are unconditional (block index clamped; none when T == 0) so
+  // that all go out before the first wait; blocks past nb count zero.
   int local[kPerThread];
+  if (nb > 0) {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) local[u] = counts[min(tid * kPerThread + u, nb - 1)];
+  }
   int sum = 0;
 #pragma unroll
   for (int u = 0; u < kPerThread; ++u) {
@@ -43,7 +49,7 @@ __global__ __launch_bounds__(kThreads) void compact_rows(int64_t T, int B, int n
     if (j < nb) {
       const int64_t rows = T - static_cast<int64_t>(j) * B;
       const int cap = rows < B ? static_cast<int>(rows) : B;
-      c = counts[j];
+      c = local[u];
       c = c < 0 ? 0 : (c > cap ? cap : c);
     }
     local[u] = c;
@@ -77,11 +83,13 @@ __global__ __launch_bounds__(kThreads) void compact_rows(int64_t T, int B, int n
     const V* s = src + (to_padded ? c : t) * vpr;
     V* d = dst + (to_padded ? t : c) * vpr;
     for (int64_t v0 = 0; v0 < vpr; v0 += kBatch * kWave) {
+      // loads unconditional (index clamped into the row) so that all go out
+      // before the first store waits; stores only in range
       V v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         const int64_t i = v0 + u * kWave + lane;
-        if (i < vpr) v[u] = s[i];
+        v[u] = s[i < vpr ? i : vpr - 1];
       }
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {

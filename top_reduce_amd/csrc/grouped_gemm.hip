@@ -74,12 +74,17 @@ struct GemmArgs {
 template <typename F>
 __device__ int expert_prefix(const int* __restrict__ counts, int E, F units, int* pre, int* tmp) {
   const int per = (E + kThreads - 1) / kThreads;
-  int u[4];
+  // the counts, loaded unconditionally (index clamped; E >= 1) so that all
+  // go out before the first wait, then masked
+  int cv[4], u[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    cv[j] = j < per ? counts[min(static_cast<int>(threadIdx.x) * per + j, E - 1)] : 0;
   int sum = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = threadIdx.x * per + j;
-    u[j] = (j < per && e < E) ? units(counts[e]) : 0;
+    u[j] = (j < per && e < E) ? units(cv[j]) : 0;
     sum += u[j];
   }
   int total = 0;
@@ -433,14 +438,29 @@ __device__ __forceinline__ TileSrc<kGather> tile_src(const GemmArgs& a, const Ti
 // their m-tiles (experts of the tiled kernel only); returns the m-tiles.
 __device__ __forceinline__ int gemm_prologue(const GemmArgs& a, int* pre, int* tmp, int* cnt_s,
                                              int* off_s) {
-  for (int e = threadIdx.x; e < a.E; e += kThreads) {
-    cnt_s[e] = a.counts[e];
-    off_s[e] = a.offsets[e];
+  // loaded unconditionally (index clamped), and stored to LDS only after
+  // the prefix has issued its own loads: one wait for memory in all
+  int cv[kMaxE / kThreads], ov[kMaxE / kThreads];
+#pragma unroll
+  for (int j = 0; j < kMaxE / kThreads; ++j) {
+    const int e = min(static_cast<int>(threadIdx.x) + j * kThreads, a.E - 1);
+    cv[j] = j * kThreads < a.E ? a.counts[e] : 0;
+    ov[j] = j * kThreads < a.E ? a.offsets[e] : 0;
   }
   const int mode = a.mode;
-  return expert_prefix(a.counts, a.E, [mode](int c) {
+  const int total_m = expert_prefix(a.counts, a.E, [mode](int c) {
     return (c > 0 && !goes_to_stream(c, mode)) ? (c + BM - 1) / BM : 0;
   }, pre, tmp);
+#pragma unroll
+  for (int j = 0; j < kMaxE / kThreads; ++j) {
+    const int e = threadIdx.x + j * kThreads;
+    if (e < a.E) {
+      cnt_s[e] = cv[j];
+      off_s[e] = ov[j];
+    }
+  }
+  __syncthreads();
+  return total_m;
 }
 
 // GEMM1 and GEMM2 of one forward in three launches, so that the blocks idle
@@ -876,13 +896,14 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
   __shared__ int tmp[kThreads / kWave];
   __shared__ floatx4 red[kThreads / kWave][2][kWave];
 
-  // the experts' segment offsets, loaded with the counts (one wait)
+  // the experts' segment offsets, loaded with the counts (one wait; indices
+  // clamped so that the loads are unconditional)
   int offv[kMaxE / kThreads], cntv[kMaxE / kThreads];
 #pragma unroll
   for (int j = 0; j < kMaxE / kThreads; ++j) {
-    const int e = threadIdx.x + j * kThreads;
-    offv[j] = e < a.E ? a.offsets[e] : 0;
-    cntv[j] = e < a.E ? a.counts[e] : 0;
+    const int e = min(static_cast<int>(threadIdx.x) + j * kThreads, a.E - 1);
+    offv[j] = j * kThreads < a.E ? a.offsets[e] : 0;
+    cntv[j] = j * kThreads < a.E ? a.counts[e] : 0;
   }
   const int mode = a.mode;
   const int n_elig = expert_prefix(a.counts, a.E, [mode](int c) {
