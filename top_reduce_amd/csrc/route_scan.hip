@@ -65,14 +65,15 @@ enum { kIgn = 0, kLocalRows = 1, kCarry = 2, kNotOne = 3 };   // offsets past E
 
 // Adds the slots and rows of rows [r0, r1) to cnt[0..hist_width(E)). Rows
 // that do not carry a token count as rows without one local slot only.
-template <typename IdxT>
-__device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1, int K,
-                           int64_t eb, int E, int B, const int* __restrict__ bc, int* cnt) {
+// expert_of(s): the local expert of slot s of a carrying row, or E.
+template <typename ExpertOf>
+__device__ void count_rows(ExpertOf expert_of, int64_t r0, int64_t r1, int K, int E, int B,
+                           const int* __restrict__ bc, int* cnt) {
   const int64_t s0 = r0 * K, s1 = r1 * K;
   for (int64_t base = s0; base < s1; base += kThreads) {
     const int64_t s = base + threadIdx.x;
     const bool in = s < s1 && (B == 0 || carries(s / K, B, bc));
-    const int e = in ? local_of(idx[s], eb, E) : E;
+    const int e = in ? expert_of(s) : E;
     if (e < E) atomicAdd(&cnt[e], 1);
     const uint64_t ign = __ballot(in && e == E);
     if (lane_id() == 0 && ign) atomicAdd(&cnt[E + kIgn], __popcll(ign));
@@ -84,7 +85,7 @@ __device__ void count_rows(const IdxT* __restrict__ idx, int64_t r0, int64_t r1,
     if (in) {
 #pragma unroll 8
       for (int k = 0; k < K; ++k) {
-        const int e = local_of(idx[r * K + k], eb, E);
+        const int e = expert_of(r * K + k);
         if (e < E) {
           ++n;
           e1 = e;
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void route_count(const IdxT* __restrict__
   __syncthreads();
   const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rpb;
   const int64_t r1 = r0 + rpb < T ? r0 + rpb : T;
-  count_rows(idx, r0, r1, K, eb, E, B, bc, cnt);
+  count_rows([&](int64_t s) { return local_of(idx[s], eb, E); }, r0, r1, K, E, B, bc, cnt);
   __syncthreads();
   for (int i = threadIdx.x; i < W; i += kThreads) hist[blockIdx.x * W + i] = cnt[i];
 }
@@ -234,11 +235,19 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     for (int u = 0; u < kPer; ++u) {
       const bool has = B == 0 ? s0 + tid + u * kThreads < s1 : pe[u] != 0;
       pe[u] = has ? local_of(pv[u], eb, E) : E;
+      const int64_t s = s0 + tid + u * kThreads;
+      if (s < s1) slot_e[s - s0] = pe[u];
     }
   }
   __syncthreads();
   if (kSelf) {
-    count_rows(idx, r0, r1, K, eb, E, B, bc, cnt);
+    // a single block counts its own slots: from the LDS slot table when it
+    // has one (with padding blocks it also needs the rows' carrying state,
+    // which the table does not keep)
+    if (cache && B == 0)
+      count_rows([&](int64_t s) { return slot_e[s - s0]; }, r0, r1, K, E, B, bc, cnt);
+    else
+      count_rows([&](int64_t s) { return local_of(idx[s], eb, E); }, r0, r1, K, E, B, bc, cnt);
   } else {
     if (hist_regs) {
       int all = 0, before = 0, sall = 0, sbefore = 0;
@@ -312,13 +321,6 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
       if (ig) atomicAdd(&misc[1], ig);
       if (lo) atomicAdd(&misc[2], lo);
       if (ca) atomicAdd(&misc[3], ca);
-    }
-  }
-  if (cache) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int64_t s = s0 + tid + u * kThreads;
-      if (s < s1) slot_e[s - s0] = pe[u];
     }
   }
   __syncthreads();
@@ -433,30 +435,40 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     const int64_t t = tb + tid;
     bool rest = false;
     if (t < r1) {
-      // this block's slots: from LDS, or from row_map and idx if too many
-      auto slot_of = [&](int k, int* e_out) {
-        const int64_t s = t * K + k;
-        if (cache) {
-          *e_out = slot_e[s - s0];
-          return slot_row[s - s0];
-        }
-        const int m = row_map[s];
-        *e_out = m >= 0 ? local_of(idx[s], eb, E) : E;
-        return m;
-      };
+      // this block's slots: from the LDS tables, or from row_map and idx if
+      // too many (two separate loops, so that the LDS reads stay LDS reads
+      // and do not become generic loads that wait for all memory)
       int n = 0, e1 = E;
-      for (int k = 0; k < K; ++k) {
-        int ek;
-        if (slot_of(k, &ek) >= 0) {
-          ++n;
-          e1 = ek;
+      bool direct;
+      if (cache) {
+        const int* se = slot_e + (t * K - s0);
+        const int* sr = slot_row + (t * K - s0);
+#pragma unroll 8
+        for (int k = 0; k < K; ++k) {
+          if (sr[k] >= 0) {
+            ++n;
+            e1 = se[k];
+          }
         }
-      }
-      const bool direct = n == 1 && cnt[e1] >= min_tiled;
-      for (int k = 0; k < K; ++k) {
-        int ek;
-        const int m = slot_of(k, &ek);
-        if (m >= 0) row_dst[m] = direct ? static_cast<int>(t * K + k) : -1;
+        direct = n == 1 && cnt[e1] >= min_tiled;
+#pragma unroll 8
+        for (int k = 0; k < K; ++k) {
+          const int m = sr[k];
+          if (m >= 0) row_dst[m] = direct ? static_cast<int>(t * K + k) : -1;
+        }
+      } else {
+        for (int k = 0; k < K; ++k) {
+          const int64_t s = t * K + k;
+          if (row_map[s] >= 0) {
+            ++n;
+            e1 = local_of(idx[s], eb, E);
+          }
+        }
+        direct = n == 1 && cnt[e1] >= min_tiled;
+        for (int k = 0; k < K; ++k) {
+          const int m = row_map[t * K + k];
+          if (m >= 0) row_dst[m] = direct ? static_cast<int>(t * K + k) : -1;
+        }
       }
       rest = !direct;
     }
