@@ -51,7 +51,7 @@ __device__ __forceinline__ int local_of(IdxT id, int64_t eb, int E) {
 // above B means all of them and one at or below 0 none.
 __device__ __forceinline__ bool carries(int64_t r, int B, const int* __restrict__ bc) {
   if (B == 0) return true;
-  const int64_t j = r / B;
+  const int64_t j = static_cast<int>(r) / B;   // r < T < 2^31
   return r - j * B < bc[j];
 }
 
@@ -72,7 +72,7 @@ __device__ void count_rows(ExpertOf expert_of, int64_t r0, int64_t r1, int K, in
   const int64_t s0 = r0 * K, s1 = r1 * K;
   for (int64_t base = s0; base < s1; base += kThreads) {
     const int64_t s = base + threadIdx.x;
-    const bool in = s < s1 && (B == 0 || carries(s / K, B, bc));
+    const bool in = s < s1 && (B == 0 || carries(static_cast<int>(s) / K, B, bc));
     const int e = in ? expert_of(s) : E;
     if (e < E) atomicAdd(&cnt[e], 1);
     const uint64_t ign = __ballot(in && e == E);
@@ -190,13 +190,13 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
           const int64_t s = s0 + tid + u * kThreads;
-          bcv[u] = bc[(s < s1 ? s : s1 - 1) / K / B];
+          bcv[u] = bc[static_cast<int>(s < s1 ? s : s1 - 1) / K / B];
         }
       }
 #pragma unroll
       for (int u = 0; u < kPer; ++u) {
         const int64_t s = s0 + tid + u * kThreads;
-        const int64_t r = s / K;
+        const int r = static_cast<int>(s) / K;
         pe[u] = s < s1 && r - r / B * B < bcv[u] ? 1 : 0;
       }
 #pragma unroll
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     const bool in = s < s1;
     const int e = !in ? E
                   : cache ? slot_e[s - s0]
-                  : (B == 0 || carries(s / K, B, bc)) ? local_of(idx[s], eb, E) : E;
+                  : (B == 0 || carries(static_cast<int>(s) / K, B, bc)) ? local_of(idx[s], eb, E) : E;
     const bool valid = e < E;
     uint64_t peers = __ballot(1);
     for (int b = 0; b < nbits; ++b) {
@@ -416,8 +416,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     if (in) {
       row_map[s] = row;
       if (valid) {
-        row_src[row] = static_cast<int>(s / K);
-        row_k[row] = static_cast<int>(s % K);
+        row_src[row] = static_cast<int>(s) / K;   // slots < T * K < 2^31: 32-bit division
+        row_k[row] = static_cast<int>(s) % K;
       }
       if (cache) slot_row[s - s0] = row;
     }
