@@ -70,10 +70,11 @@ struct GemmArgs {
 };
 
 // Builds in LDS the exclusive prefix of `units(e)` over experts; returns the
-// total. `pre` has E+1 entries, `tmp` kThreads/64.
-template <typename F>
+// total. `pre` has E+1 entries, `tmp` kBlock/64; E <= 4 kBlock.
+template <int kBlock = kThreads, typename F>
 __device__ int expert_prefix(const int* __restrict__ counts, int E, F units, int* pre, int* tmp) {
-  const int per = (E + kThreads - 1) / kThreads;
+  static_assert(4 * kBlock >= kMaxE, "four experts per thread");
+  const int per = (E + kBlock - 1) / kBlock;
   // the counts, loaded unconditionally (index clamped; E >= 1) so that all
   // go out before the first wait, then masked
   int cv[4], u[4];
@@ -88,7 +89,7 @@ __device__ int expert_prefix(const int* __restrict__ counts, int E, F units, int
     sum += u[j];
   }
   int total = 0;
-  int off = block_exclusive_scan<kThreads>(sum, tmp, &total);
+  int off = block_exclusive_scan<kBlock>(sum, tmp, &total);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = threadIdx.x * per + j;
@@ -1024,6 +1025,149 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
 }
 
 // --------------------------------------------------------------------------
+// Decode kernel (bf16; a batch of at most kStreamMaxRows expanded rows)
+// --------------------------------------------------------------------------
+// One decode step streams each active expert's weights once against a row or
+// a few: its time is the read latency of the weights more than their
+// bandwidth, and there are few units (one expert's 2I / 8 or H / 16), about
+// one per CU. Units as in gemm_stream, the reduction split over kDecWaves
+// waves; a wave issues every load of its share (kDecB k32 blocks at a time)
+// and waits once, so a unit's weight bytes are in flight together. Token
+// rows go in groups of 16, one after another (a decode expert rarely has
+// more than 16).
+constexpr int kDecWaves = 8;
+constexpr int kDecThreads = kDecWaves * kWave;
+
+// kDecB: k32 blocks per chunk (8 or 16, the launch picks the one that fits a
+// wave's share with the fewest spare loads).
+template <bool kSwiglu, int kDecB>
+__global__ __launch_bounds__(kDecThreads) void gemm_decode(GemmArgs a, int I) {
+  __shared__ int pre[kMaxE + 1];
+  __shared__ int list[kMaxE];
+  __shared__ int cnt_s[kMaxE], off_s[kMaxE];
+  __shared__ int tmp[kDecWaves];
+  __shared__ floatx4 red[kDecWaves][kWave];
+
+  // the experts' counts and offsets, loaded together with the prefix's
+  int offv[kMaxE / kDecThreads], cntv[kMaxE / kDecThreads];
+#pragma unroll
+  for (int j = 0; j < kMaxE / kDecThreads; ++j) {
+    const int e = min(static_cast<int>(threadIdx.x) + j * kDecThreads, a.E - 1);
+    offv[j] = j * kDecThreads < a.E ? a.offsets[e] : 0;
+    cntv[j] = j * kDecThreads < a.E ? a.counts[e] : 0;
+  }
+  const int mode = a.mode;
+  const int n_elig = expert_prefix<kDecThreads>(a.counts, a.E, [mode](int c) {
+    return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
+  }, pre, tmp);
+  if (n_elig == 0) return;
+#pragma unroll
+  for (int j = 0; j < kMaxE / kDecThreads; ++j) {
+    const int e = threadIdx.x + j * kDecThreads;
+    if (e < a.E) {
+      if (pre[e + 1] > pre[e]) list[pre[e]] = e;
+      cnt_s[e] = cntv[j];
+      off_s[e] = offv[j];
+    }
+  }
+  __syncthreads();
+
+  const int cols = kSwiglu ? 8 : 16;               // outputs per unit
+  const int upe = (a.Nc + cols - 1) / cols;        // units per expert
+  const int total = n_elig * upe;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;                         // k group of the lane
+  const int arow = lane & 15;                      // operand row of the lane
+  const int Kd = a.Kd;
+  const int nk32 = Kd / 32;
+  const int kb0 = wave * nk32 / kDecWaves, kb1 = (wave + 1) * nk32 / kDecWaves;
+  const int64_t Nb = kSwiglu ? 2 * static_cast<int64_t>(I) : a.Nc;
+  const uint16_t* __restrict__ Ab = static_cast<const uint16_t*>(a.A);
+  const uint16_t* __restrict__ Bb = static_cast<const uint16_t*>(a.B);
+  uint16_t* __restrict__ Cb = static_cast<uint16_t*>(a.C);
+
+  for (int u = blockIdx.x; u < total; u += gridDim.x) {
+    const int e = list[u / upe];
+    const int c = u % upe;
+    const int cnt = cnt_s[e];
+    const int off = off_s[e];
+    int64_t wrow;
+    if (kSwiglu) {
+      const int col = min(c * 8 + (arow & 7), I - 1);
+      wrow = arow < 8 ? col : I + col;
+    } else {
+      wrow = min(c * 16 + arow, a.Nc - 1);
+    }
+    const uint16_t* wp = Bb + (static_cast<int64_t>(e) * Nb + wrow) * Kd + g * 8;
+
+    for (int tb = 0; tb < cnt; tb += 16) {
+      const int tok = tb + arow;
+      const bool xv = tok < cnt;
+      const int r = off + (xv ? tok : 0);
+      const int row = a.gather ? a.gather[r] : r;
+      floatx4 acc = {0, 0, 0, 0};
+      for (int kb = kb0; kb < kb1; kb += kDecB) {
+        // every load of the chunk first, then one wait. The weight loads are
+        // unconditional (blocks past the share re-read its last block, and
+        // their MFMAs are skipped), so the compiler can count them and wait
+        // for the row id below without waiting for them.
+        u32x4 wa[kDecB], xb[kDecB];
+#pragma unroll
+        for (int j = 0; j < kDecB; ++j)
+          wa[j] = *reinterpret_cast<const u32x4*>(wp + min(kb + j, kb1 - 1) * 32);
+        // the token row's id is used only after the weight loads are out (the
+        // empty asm takes it here and keeps the loads before it), so its
+        // gather overlaps the weights' latency
+        int rr = row;
+        asm volatile("" : "+v"(rr) : : "memory");
+        const uint16_t* xp = Ab + static_cast<int64_t>(rr) * Kd + g * 8;
+#pragma unroll
+        for (int j = 0; j < kDecB; ++j)
+          if (kb + j < kb1)
+            xb[j] = xv ? *reinterpret_cast<const u32x4*>(xp + (kb + j) * 32) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < kDecB; ++j)
+          if (kb + j < kb1)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[j]),
+                                                          __builtin_bit_cast(bf16x8, xb[j]), acc,
+                                                          0, 0, 0);
+      }
+      red[wave][lane] = acc;
+      __syncthreads();
+      if (wave == 0) {
+        // the waves' partial sums in a fixed order; lane (g, r) holds output
+        // columns 4 g .. 4 g + 3 of the unit for token tb + r, lane + 16 the
+        // next four, and lanes of even g store 8 columns with one 16-byte
+        // store (I % 128 == 0, H % 256 == 0)
+        floatx4 s = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < kDecWaves; ++w) s += red[w][lane];
+        uint32_t p0, p1;
+        if (kSwiglu) {
+          // lanes 0..31 hold gate rows, lanes 32..63 the matching up rows
+          floatx4 up = red[0][lane ^ 32];
+#pragma unroll
+          for (int w = 1; w < kDecWaves; ++w) up += red[w][lane ^ 32];
+          p0 = pack_bf16x2(silu_mul(s[0], up[0]), silu_mul(s[1], up[1]));
+          p1 = pack_bf16x2(silu_mul(s[2], up[2]), silu_mul(s[3], up[3]));
+        } else {
+          p0 = pack_bf16x2(s[0], s[1]);
+          p1 = pack_bf16x2(s[2], s[3]);
+        }
+        const uint32_t n0 = __shfl_down(p0, 16, kWave), n1 = __shfl_down(p1, 16, kWave);
+        const bool st = kSwiglu ? g == 0 : (g & 1) == 0;
+        const int col = kSwiglu ? c * 8 : c * 16 + 4 * g;
+        if (st && xv && col + 8 <= a.Nc)
+          *reinterpret_cast<u32x4*>(Cb + static_cast<int64_t>(off + tok) * a.Nc + col) =
+              u32x4{p0, p1, n0, n1};
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // fp32 kernel: fp32 MFMA (v_mfma_f32_16x16x4_f32), one wave per 16-row x
 // 16-output tile
 // --------------------------------------------------------------------------
@@ -1218,8 +1362,22 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
                          static_cast<int>(kPartAll), 0);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  // A decode batch (AUTO mode, at most kStreamMaxRows expanded rows, so no
+  // tiled experts): the latency-minded kernel, one block per unit up to one
+  // per CU.
+  const bool decode = !tiled && mode == kModeAuto;
+  const unsigned gd1 = static_cast<unsigned>(u1 < cus ? u1 : cus);
+  const unsigned gd2 = static_cast<unsigned>(u2 < cus ? u2 : cus);
+  // each wave's share of k32 blocks: chunks of 8 when it fits, else 16
+  const bool dec8_up = cdiv(cdiv(d.H, 32), kDecWaves) <= 8;
+  const bool dec8_down = cdiv(cdiv(I, 32), kDecWaves) <= 8;
   if (up && mode != kModeTiled) {
-    hipLaunchKernelGGL(gemm_stream<true>, dim3(gs1), dim3(kThreads), 0, st, g1, I);
+    if (decode && dec8_up)
+      hipLaunchKernelGGL((gemm_decode<true, 8>), dim3(gd1), dim3(kDecThreads), 0, st, g1, I);
+    else if (decode)
+      hipLaunchKernelGGL((gemm_decode<true, 16>), dim3(gd1), dim3(kDecThreads), 0, st, g1, I);
+    else
+      hipLaunchKernelGGL(gemm_stream<true>, dim3(gs1), dim3(kThreads), 0, st, g1, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (down && tiled) {
@@ -1228,7 +1386,12 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (down && mode != kModeTiled) {
-    hipLaunchKernelGGL(gemm_stream<false>, dim3(gs2), dim3(kThreads), 0, st, g2, I);
+    if (decode && dec8_down)
+      hipLaunchKernelGGL((gemm_decode<false, 8>), dim3(gd2), dim3(kDecThreads), 0, st, g2, I);
+    else if (decode)
+      hipLaunchKernelGGL((gemm_decode<false, 16>), dim3(gd2), dim3(kDecThreads), 0, st, g2, I);
+    else
+      hipLaunchKernelGGL(gemm_stream<false>, dim3(gs2), dim3(kThreads), 0, st, g2, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;
