@@ -110,9 +110,14 @@ typedef struct tr_moe_plan {
     int32_t* row_map;      /* [T*K] expanded row of slot (t,k), or -1 */
     int32_t* row_src;      /* [R_cap] received row of expanded row r (r < R) */
     int32_t* row_k;        /* [R_cap] slot of expanded row r (r < R) */
-    int32_t* stats;        /* [6] R, rows with >= 1 local route, ignored slots, empty
+    int32_t* stats;        /* [8] R, rows with >= 1 local route, ignored slots, empty
                               experts, entries of tok_rest, rows that carry a
-                              token (T, or the carrying rows of a padded plan) */
+                              token (T, or the carrying rows of a padded plan),
+                              non-empty experts the streaming GEMM takes (fewer
+                              than 33 routes; every one with
+                              TR_FLAG_GEMM_FORCE_STREAM, none with
+                              TR_FLAG_GEMM_FORCE_TILED), non-empty experts the
+                              tiled GEMM takes (the others) */
     int32_t* scan_tmp;     /* route-scan block partials */
     void* Xe;              /* [R_cap + 256, H] expanded rows (expert-contiguous);
                               NULL with TR_FLAG_NO_XE */

@@ -48,6 +48,12 @@ def _check_route(idx_np, E, B, counts, idx_dtype=torch.int64, flags=0):
     assert stats == (R, int(local.any(1).sum()), int(foreign.sum()),
                      int((ref["counts"] == 0).sum()))
     assert int(v["stats"][5]) == int(carry.sum())
+    # experts of the streaming and of the tiled GEMM, per the plan's mode
+    c = ref["counts"]
+    lo = (1 if flags & tr.FLAG_GEMM_FORCE_TILED
+          else np.iinfo(np.int64).max if flags & tr.FLAG_GEMM_FORCE_STREAM else 33)
+    assert int(v["stats"][6]) == int(((c > 0) & (c < lo)).sum())
+    assert int(v["stats"][7]) == int((c >= lo).sum())
     # padding rows are among the rows the reduce writes (as +0)
     n_rest = int(v["stats"][4])
     rest_rows = v["tok_rest"][:n_rest].cpu().numpy()
@@ -97,6 +103,12 @@ def test_padded_route_edge_cases():
     # 64 experts over ~254 scan blocks (batched partial sums)
     T, B = 20000, 96
     _check_route(rng.integers(-1, 64, size=(T, 8)), 64, B, rng.integers(0, B + 1, size=-(-T // B)))
+    # the GEMM modes' expert counts (experts with 1..32 and with more routes)
+    T, B = 3000, 50
+    idx = np.where(rng.random((T, 4)) < 0.02, rng.integers(0, 40, size=(T, 4)),
+                   rng.integers(40, 48, size=(T, 4)))
+    for fl in (0, tr.FLAG_GEMM_FORCE_TILED, tr.FLAG_GEMM_FORCE_STREAM):
+        _check_route(idx, 48, B, rng.integers(0, B + 1, size=-(-T // B)), flags=fl)
 
 
 @pytest.fixture(scope="module")

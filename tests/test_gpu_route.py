@@ -48,6 +48,10 @@ def _check(idx_np, E, eb=0, idx_dtype=torch.int64, H=256, I=128):
     local = (idx_np >= eb) & (idx_np < eb + E)
     assert stats == (R, int(local.any(1).sum()) if T else 0, int((~local).sum()),
                      int((ref["counts"] == 0).sum()))
+    # experts of the streaming GEMM (1..32 routes) and of the tiled GEMM (> 32)
+    c = ref["counts"]
+    assert int(v["stats"][6]) == int(((c > 0) & (c <= 32)).sum())
+    assert int(v["stats"][7]) == int((c > 32).sum())
 
 
 @pytest.mark.parametrize("name,T", [("c1", None), ("c2", None), ("c3", 1), ("c3", 8), ("c3", 64),

@@ -207,7 +207,7 @@ class MoePlan:
             row_k=self._view(s.row_k, s.R_cap, torch.int32, (s.R_cap,)),
             row_dst=self._view(s.row_dst, s.R_cap, torch.int32, (s.R_cap,)),
             tok_rest=self._view(s.tok_rest, d.T, torch.int32, (d.T,)),
-            stats=self._view(s.stats, 6, torch.int32, (6,)),
+            stats=self._view(s.stats, 8, torch.int32, (8,)),
             Xe=None if not s.Xe else self._view(s.Xe, s.R_cap * d.H, dt, (s.R_cap, d.H)),
             h=self._view(s.h, s.R_cap * d.I, dt, (s.R_cap, d.I)),
             O=self._view(s.O, s.R_cap * d.H, dt, (s.R_cap, d.H)),

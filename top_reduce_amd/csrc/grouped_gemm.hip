@@ -67,6 +67,11 @@ struct GemmArgs {
   void* y;              // [T, Nc]
   int K;
   int64_t T;
+  // the number of experts this launch's kernel takes, counted by the route
+  // scan (plan stats 6: streaming, 7: tiled); a launch with none exits after
+  // its first loads. Read by gemm_tiled, gemm_hybrid and gemm_stream (never
+  // NULL for them).
+  const int* n_take;
 };
 
 // Builds in LDS the exclusive prefix of `units(e)` over experts; returns the
@@ -436,9 +441,12 @@ __device__ __forceinline__ TileSrc<kGather> tile_src(const GemmArgs& a, const Ti
 
 #if defined(__HIP_DEVICE_COMPILE__)
 // The experts' counts and segment offsets copied to LDS, and the prefix of
-// their m-tiles (experts of the tiled kernel only); returns the m-tiles.
+// their m-tiles (experts of the tiled kernel only); returns the m-tiles, or
+// -1 without touching LDS when the route scan counted no expert for the
+// launch (a.n_take).
 __device__ __forceinline__ int gemm_prologue(const GemmArgs& a, int* pre, int* tmp, int* cnt_s,
                                              int* off_s) {
+  const int take = *a.n_take;
   // loaded unconditionally (index clamped), and stored to LDS only after
   // the prefix has issued its own loads: one wait for memory in all
   int cv[kMaxE / kThreads], ov[kMaxE / kThreads];
@@ -448,6 +456,8 @@ __device__ __forceinline__ int gemm_prologue(const GemmArgs& a, int* pre, int* t
     cv[j] = j * kThreads < a.E ? a.counts[e] : 0;
     ov[j] = j * kThreads < a.E ? a.offsets[e] : 0;
   }
+  asm volatile("" : : : "memory");   // the loads above go out before the exit test
+  if (take == 0) return -1;
   const int mode = a.mode;
   const int total_m = expert_prefix(a.counts, a.E, [mode](int c) {
     return (c > 0 && !goes_to_stream(c, mode)) ? (c + BM - 1) / BM : 0;
@@ -801,6 +811,7 @@ __global__ __launch_bounds__(kThreads) void gemm_tiled(GemmArgs a, int I, int pa
   __shared__ int tmp[kWavesT];
   __shared__ int cnt_s[kMaxE], off_s[kMaxE];
   const int total_m = gemm_prologue(a, pre, tmp, cnt_s, off_s);
+  if (total_m < 0) return;
   constexpr int kOutCols = kSwiglu ? BN / 2 : BN;
   const int NT = (a.Nc + kOutCols - 1) / kOutCols;
   const int total = total_m * NT;
@@ -828,6 +839,7 @@ __global__ __launch_bounds__(kThreads) void gemm_hybrid(GemmArgs g1, GemmArgs g2
   __shared__ int tmp[kWavesT];
   __shared__ int cnt_s[kMaxE], off_s[kMaxE];
   const int total_m = gemm_prologue(g1, pre, tmp, cnt_s, off_s);
+  if (total_m < 0) return;
   const int NT1 = (g1.Nc + BN / 2 - 1) / (BN / 2), NT2 = (g2.Nc + BN - 1) / BN;
   const int G = gridDim.x;
   const int total1 = total_m * NT1;
@@ -898,7 +910,9 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
   __shared__ floatx4 red[kThreads / kWave][2][kWave];
 
   // the experts' segment offsets, loaded with the counts (one wait; indices
-  // clamped so that the loads are unconditional)
+  // clamped so that the loads are unconditional); a launch for which the
+  // route scan counted no expert (a.n_take) exits before the prefix
+  const int take = *a.n_take;
   int offv[kMaxE / kThreads], cntv[kMaxE / kThreads];
 #pragma unroll
   for (int j = 0; j < kMaxE / kThreads; ++j) {
@@ -906,6 +920,8 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
     offv[j] = j * kThreads < a.E ? a.offsets[e] : 0;
     cntv[j] = j * kThreads < a.E ? a.counts[e] : 0;
   }
+  asm volatile("" : : : "memory");   // the loads above go out before the exit test
+  if (take == 0) return;
   const int mode = a.mode;
   const int n_elig = expert_prefix(a.counts, a.E, [mode](int c) {
     return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
@@ -1292,6 +1308,11 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     g2.y = y_fused;
   }
   hipError_t err;
+  // the route scan's counts of the experts each bf16 kernel takes: a launch
+  // that finds none exits after one load
+  GemmArgs g1t = g1, g2t = g2, g1s = g1, g2s = g2;
+  g1t.n_take = g2t.n_take = p.stats + 7;
+  g1s.n_take = g2s.n_take = p.stats + 6;
 
   if (d.dtype == TR_F32) {
     // one tile per wave, four waves per block
@@ -1329,36 +1350,36 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   if (split) {
     const unsigned gsplit = gt1;
     if (g1.gather)
-      hipLaunchKernelGGL((gemm_tiled<true, true>), dim3(gsplit), dim3(kThreads), 0, st, g1, I,
+      hipLaunchKernelGGL((gemm_tiled<true, true>), dim3(gsplit), dim3(kThreads), 0, st, g1t, I,
                          static_cast<int>(kPartWholeRounds), 0);
     else
-      hipLaunchKernelGGL((gemm_tiled<true, false>), dim3(gsplit), dim3(kThreads), 0, st, g1, I,
+      hipLaunchKernelGGL((gemm_tiled<true, false>), dim3(gsplit), dim3(kThreads), 0, st, g1t, I,
                          static_cast<int>(kPartWholeRounds), 0);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (mode != kModeTiled) {
-      hipLaunchKernelGGL(gemm_stream<true>, dim3(gs1), dim3(kThreads), 0, st, g1, I);
+      hipLaunchKernelGGL(gemm_stream<true>, dim3(gs1), dim3(kThreads), 0, st, g1s, I);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (g1.gather)
-      hipLaunchKernelGGL((gemm_hybrid<true>), dim3(gsplit), dim3(kThreads), 0, st, g1, g2, I);
+      hipLaunchKernelGGL((gemm_hybrid<true>), dim3(gsplit), dim3(kThreads), 0, st, g1t, g2t, I);
     else
-      hipLaunchKernelGGL((gemm_hybrid<false>), dim3(gsplit), dim3(kThreads), 0, st, g1, g2, I);
+      hipLaunchKernelGGL((gemm_hybrid<false>), dim3(gsplit), dim3(kThreads), 0, st, g1t, g2t, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL((gemm_tiled<false, false>), dim3(gt2), dim3(kThreads), 0, st, g2, I,
+    hipLaunchKernelGGL((gemm_tiled<false, false>), dim3(gt2), dim3(kThreads), 0, st, g2t, I,
                        static_cast<int>(kPartRest), static_cast<int>(gsplit));
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (mode != kModeTiled) {
-      hipLaunchKernelGGL(gemm_stream<false>, dim3(gs2), dim3(kThreads), 0, st, g2, I);
+      hipLaunchKernelGGL(gemm_stream<false>, dim3(gs2), dim3(kThreads), 0, st, g2s, I);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;
   }
   if (up && tiled) {
     if (g1.gather)
-      hipLaunchKernelGGL((gemm_tiled<true, true>), dim3(gt1), dim3(kThreads), 0, st, g1, I,
+      hipLaunchKernelGGL((gemm_tiled<true, true>), dim3(gt1), dim3(kThreads), 0, st, g1t, I,
                          static_cast<int>(kPartAll), 0);
     else
-      hipLaunchKernelGGL((gemm_tiled<true, false>), dim3(gt1), dim3(kThreads), 0, st, g1, I,
+      hipLaunchKernelGGL((gemm_tiled<true, false>), dim3(gt1), dim3(kThreads), 0, st, g1t, I,
                          static_cast<int>(kPartAll), 0);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -1377,11 +1398,11 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     else if (decode)
       hipLaunchKernelGGL((gemm_decode<true, 16>), dim3(gd1), dim3(kDecThreads), 0, st, g1, I);
     else
-      hipLaunchKernelGGL(gemm_stream<true>, dim3(gs1), dim3(kThreads), 0, st, g1, I);
+      hipLaunchKernelGGL(gemm_stream<true>, dim3(gs1), dim3(kThreads), 0, st, g1s, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (down && tiled) {
-    hipLaunchKernelGGL((gemm_tiled<false, false>), dim3(gt2), dim3(kThreads), 0, st, g2, I,
+    hipLaunchKernelGGL((gemm_tiled<false, false>), dim3(gt2), dim3(kThreads), 0, st, g2t, I,
                        static_cast<int>(kPartAll), 0);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
@@ -1391,7 +1412,7 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     else if (decode)
       hipLaunchKernelGGL((gemm_decode<false, 16>), dim3(gd2), dim3(kDecThreads), 0, st, g2, I);
     else
-      hipLaunchKernelGGL(gemm_stream<false>, dim3(gs2), dim3(kThreads), 0, st, g2, I);
+      hipLaunchKernelGGL(gemm_stream<false>, dim3(gs2), dim3(kThreads), 0, st, g2s, I);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   return hipSuccess;

@@ -39,6 +39,7 @@ constexpr int kWaves = kThreads / kWave;
 // A block keeps each of its slots' local expert and expanded row in LDS for
 // the last phase when it has at most this many slots (else it re-reads them).
 constexpr int kSlotCache = 2048;
+constexpr int kMisc = 10;          // block-wide counters of the scatter kernel
 
 template <typename IdxT>
 __device__ __forceinline__ int local_of(IdxT id, int64_t eb, int E) {
@@ -140,13 +141,14 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   int* wcnt = running + E;              // [kWaves][E + 1] per-wave counts of a round
   int* cnt = wcnt + kWaves * (E + 1);   // [W] totals over the blocks (own counts: kSelf)
   int* tmp = cnt + W;                   // [kWaves] scan scratch
-  int* misc = tmp + kWaves;             // [8]
-  int* slot_e = misc + 8;               // [kSlotCache] local expert of each slot (E: none)
+  int* misc = tmp + kWaves;             // [kMisc]
+  int* slot_e = misc + kMisc;           // [kSlotCache] local expert of each slot (E: none)
   int* slot_row = slot_e + kSlotCache;  // [kSlotCache] its expanded row (-1: none)
   // misc: [0] empty experts, [1] ignored slots, [2] rows with a local slot,
   // [3] carrying rows, [4] rows without one local slot in earlier blocks,
   // [5] the same over all blocks, [6] / [7] rows whose one local slot goes
-  // to a streamed expert, in earlier blocks / in all blocks
+  // to a streamed expert, in earlier blocks / in all blocks, [8] / [9]
+  // experts the streaming / the tiled GEMM takes
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   int* sprior = wcnt + E;               // [E] likewise: one-slot rows in earlier blocks
   for (int i = tid; i < W; i += kThreads) cnt[i] = 0;
   for (int i = tid; i < 2 * E; i += kThreads) prior[i] = 0;
-  if (tid < 8) misc[tid] = 0;
+  if (tid < kMisc) misc[tid] = 0;
   const int64_t s0 = r0 * K, s1 = r1 * K;
   const bool cache = s1 - s0 <= kSlotCache;
   // The local expert of each of this block's slots (E: none), kept in LDS
@@ -366,6 +368,7 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
         counts[e] = tot[j];
         offsets[e] = off;
         if (tot[j] == 0) atomicAdd(&misc[0], 1);
+        else atomicAdd(&misc[tot[j] < min_tiled ? 8 : 9], 1);
       }
       off += tot[j];
     }
@@ -379,6 +382,8 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
     stats[3] = misc[0];
     stats[4] = (kSelf ? cnt[E + kNotOne] : misc[5]) + misc[7];
     stats[5] = kSelf ? cnt[E + kCarry] : misc[3];
+    stats[6] = misc[8];
+    stats[7] = misc[9];
   }
   int rest_at = kSelf ? 0 : misc[4] + misc[6];
 
@@ -492,7 +497,7 @@ hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
   const int E = d.E, K = d.K;
   const int nb = p.scan_blocks, rpb = p.scan_rows_per_block;
   const size_t sh_scatter =
-      sizeof(int) * (2 * E + kWaves * (E + 1) + hist_width(E) + kWaves + 8 + 2 * kSlotCache);
+      sizeof(int) * (2 * E + kWaves * (E + 1) + hist_width(E) + kWaves + kMisc + 2 * kSlotCache);
   const int B = p.block_rows;
   const int* bc = p.block_counts;
   // fewest routes of an expert the grouped GEMM tiles (the others stream)
