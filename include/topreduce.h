@@ -36,9 +36,12 @@
  *    Calls are graph-capturable except moe_plan_stats.
  *  - Arrays are dense and row-major. x, y, W1, W2 and the expert buffers are
  *    all of one element type, desc->dtype.
- *  - Shapes: bf16 needs H a multiple of 256 and I a multiple of 128 (whole
- *    GEMM tiles along the output columns); fp32 needs H a multiple of 8.
- *    Other shapes return TR_EUNSUPPORTED.
+ *  - Shapes: H a multiple of 8 (rows of x, y and the expert buffers move in
+ *    16-byte pieces), any I; other H return TR_EUNSUPPORTED. bf16 shapes with
+ *    H a multiple of 256 and I a multiple of 128 run the tiled / streaming
+ *    GEMM kernels; the others run one any-shape kernel for both GEMMs (32 x 32
+ *    tiles per wave, operands from L2; the GEMM force flags then only change
+ *    which rows the reduce folded into GEMM2 takes).
  *  - Errors: a non-zero tr_status and a message in moe_last_error(). Argument
  *    checks happen on the host before anything is enqueued. Nothing aborts.
  *  - Ids outside [expert_begin, expert_begin + E), -1 included, are routes to

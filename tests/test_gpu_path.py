@@ -24,6 +24,13 @@ gen.custom_spec("mid_f32", T=300, K=4, E=6, G=12, H=264, I=72, dtype="f32", zipf
 # fp32 with I not a multiple of 4 (ragged k tail of GEMM2, ragged output
 # columns of GEMM1) and H not a multiple of 16
 gen.custom_spec("odd_f32", T=200, K=3, E=5, G=9, H=136, I=70, dtype="f32", zipf_s=0.5, seed=12)
+# bf16 shapes off the tiled kernel's 256 / 128 column grid (the any-shape
+# kernel): H % 256 != 0 with I a multiple of 8; I not a multiple of 8 (GEMM2's
+# k tail loaded element-wise, GEMM1's last output columns stored one by one);
+# an H and I of a published expert shape's size class (2880 / 1440)
+gen.custom_spec("odd_bf16", T=300, K=4, E=6, G=12, H=264, I=72, zipf_s=0.5, seed=13)
+gen.custom_spec("odd_i_bf16", T=200, K=3, E=5, G=9, H=136, I=70, zipf_s=0.5, seed=14)
+gen.custom_spec("wide_bf16", T=128, K=4, E=8, G=16, H=2880, I=1440, zipf_s=1.0, seed=15)
 # every row routes to all 8 experts: 8 segments of 2080 rows, 9 m-tiles each
 # (the last one 32 rows deep); 288 tiles per GEMM, more than one round of the
 # persistent grid on 256 compute units.
@@ -53,7 +60,10 @@ def _forward(wl, flags=0, y_alias=False, weights=True):
                                         ("rounds", 0),
                                         ("mid", tr.FLAG_GEMM_FORCE_TILED),
                                         ("mid", tr.FLAG_GEMM_FORCE_STREAM),
-                                        ("mid_small_experts", 0)])
+                                        ("mid_small_experts", 0),
+                                        ("odd_bf16", 0), ("odd_i_bf16", 0), ("wide_bf16", 0),
+                                        ("odd_bf16", tr.FLAG_GEMM_FORCE_TILED),
+                                        ("odd_bf16", tr.FLAG_GEMM_FORCE_STREAM)])
 def test_forward_full_compare(name, flags):
     say(f"forward {name} flags={flags}")
     wl = gen.make_workload(name, with_weights=True)
@@ -97,7 +107,7 @@ def test_forward_full_size_sampled(name):
     _assert_close(as_f64(y[toks]), ref, wl.dtype, f"{name} y[{len(toks)} rows]")
 
 
-@pytest.mark.parametrize("name", ["mid", "c1", "rounds"])
+@pytest.mark.parametrize("name", ["mid", "c1", "rounds", "odd_i_bf16"])
 def test_stages(name):
     """expand bit-exact; O rows vs the oracle's per-route MLP; reduce."""
     say(f"stages {name}")
@@ -172,9 +182,10 @@ def test_all_padding_gives_positive_zero():
     assert (y == 0).all()          # +0 bits
 
 
-def test_y_aliases_x():
-    say("y aliases x")
-    wl = gen.make_workload("mid", with_weights=True)
+@pytest.mark.parametrize("name", ["mid", "odd_bf16"])
+def test_y_aliases_x(name):
+    say(f"y aliases x {name}")
+    wl = gen.make_workload(name, with_weights=True)
     _, y_sep = _forward(wl)
     _, y_al = _forward(wl, y_alias=True)
     assert np.array_equal(y_sep, y_al)
@@ -203,7 +214,7 @@ def test_error_convention_on_device():
 @pytest.mark.parametrize("name,flags", [("mid", 0), ("mid", tr.FLAG_GEMM_FORCE_TILED),
                                         ("mid", tr.FLAG_GEMM_FORCE_STREAM),
                                         ("mid_small_experts", 0), ("mid_f32", 0), ("c1", 0),
-                                        ("rounds", 0)])
+                                        ("rounds", 0), ("odd_bf16", 0), ("odd_i_bf16", 0)])
 def test_up_x_equals_expand_then_up(name, flags):
     """GEMM1 gathering the received rows through the route table computes the
     same h, bit for bit, as expand followed by GEMM1 over Xe: the same rows
@@ -249,7 +260,9 @@ def test_up_x_decode(T):
                                           ("mid_small_experts", 0, None), ("rounds", 0, None),
                                           ("split", 0, None),
                                           ("c3", 0, 1), ("c3", 0, 64), ("c4", 0, None),
-                                          ("c2", 0, None), ("c5", 0, None)])
+                                          ("c2", 0, None), ("c5", 0, None),
+                                          ("odd_bf16", 0, None), ("wide_bf16", 0, None),
+                                          ("odd_i_bf16", tr.FLAG_GEMM_FORCE_TILED, None)])
 def test_forward_fused_equals_stages(name, flags, T):
     """moe_forward (GEMM1 gathering x, GEMM2 writing rows of received rows
     with one local slot straight to y, the reduce for the rest) equals the

@@ -50,13 +50,8 @@ tr_status check_desc(const tr_moe_desc* d) {
   if (d->T > (int64_t(1) << 31) / d->K) return fail(TR_EUNSUPPORTED, "T*K must be < 2^31");
   if (d->expert_begin > (int64_t(1) << 62) || d->expert_begin < -(int64_t(1) << 62))
     return fail(TR_EINVAL, "expert_begin out of range");
-  if (d->dtype == TR_BF16) {
-    if (d->H % tr::kColMultiple || d->I % (tr::kColMultiple / 2))
-      return fail(TR_EUNSUPPORTED, "bf16 needs H a multiple of %d and I of %d (got H=%lld I=%lld)",
-                  tr::kColMultiple, tr::kColMultiple / 2, (long long)d->H, (long long)d->I);
-  } else {
-    if (d->H % 8) return fail(TR_EUNSUPPORTED, "fp32 needs H a multiple of 8 (got %lld)", (long long)d->H);
-  }
+  // rows of x, y, Xe and O move in 16-byte pieces
+  if (d->H % 8) return fail(TR_EUNSUPPORTED, "H must be a multiple of 8 (got %lld)", (long long)d->H);
   // without an expanded buffer GEMM1 must be able to gather from x
   if ((d->flags & TR_FLAG_NO_XE) && !tr::gemm_can_gather(*d))
     return fail(TR_EUNSUPPORTED, "TR_FLAG_NO_XE needs bf16 and T * H * 2 < 2^31");

@@ -1274,6 +1274,148 @@ __global__ __launch_bounds__(kThreads) void gemm_f32(GemmArgs a, int I) {
   }
 }
 
+
+// --------------------------------------------------------------------------
+// bf16 kernel for any H (a multiple of 8) and any I: the shapes whose output
+// columns do not fill the tiled kernel's 256-column tiles (H % 256 or
+// I % 128 non-zero). One wave per 32-column x 32-row output tile, operands
+// straight from global memory (L2), v_mfma_f32_16x16x32_bf16.
+// --------------------------------------------------------------------------
+// A 16x16x32 MFMA takes from lane l eight consecutive k of A row l % 16 and of
+// B column l % 16, k group l / 16, and leaves in lane l the outputs (rows
+// 4 (l / 16) + 0..3, column l % 16). Here A is the weights (rows = output
+// columns) and B the activations (columns = tokens), so a lane ends with four
+// consecutive output columns of one token. Rows of the weights or tokens past
+// their end and k past Kd load as zero; k runs in 32-wide steps, four per
+// batch of loads. GEMM1 may read its rows through `gather`; GEMM2 may send a
+// row with a fused slot (dst >= 0) to y as fma(w, bf16 output, +0), rounded
+// once, exactly as the tiled kernel's fused epilogue does.
+constexpr int G_BM = 32, G_BN = 32;
+
+template <bool kSwiglu>
+__global__ __launch_bounds__(kThreads) void gemm_any(GemmArgs a, int I) {
+  __shared__ int pre[kMaxE + 1];
+  __shared__ int tmp[kThreads / kWave];
+
+  const int total_m = expert_prefix(a.counts, a.E, [](int c) {
+    return c > 0 ? (c + G_BM - 1) / G_BM : 0;
+  }, pre, tmp);
+  const int NT = (a.Nc + G_BN - 1) / G_BN;
+  const int total = total_m * NT;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int Kd = a.Kd;
+  const bool vec = (Kd & 7) == 0;   // rows start 16-byte aligned
+  const int64_t Nb = kSwiglu ? 2 * static_cast<int64_t>(I) : a.Nc;
+  const uint16_t* __restrict__ Ab = static_cast<const uint16_t*>(a.A);
+  const uint16_t* __restrict__ Bb = static_cast<const uint16_t*>(a.B);
+  uint16_t* __restrict__ Cb = static_cast<uint16_t*>(a.C);
+  uint16_t* __restrict__ Yb = static_cast<uint16_t*>(a.y);
+
+  // eight bf16 of row p at k .. k + 7 (k a multiple of 8), zero past Kd
+  // (p == nullptr: zero)
+  auto load8 = [Kd, vec](const uint16_t* p, int k) -> u32x4 {
+    if (p && vec && k < Kd) return *reinterpret_cast<const u32x4*>(p + k);
+    u32x4 w = {0, 0, 0, 0};
+    if (p) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = k + 2 * i < Kd ? p[k + 2 * i] : 0;
+        const uint32_t hi = k + 2 * i + 1 < Kd ? p[k + 2 * i + 1] : 0;
+        w[i] = lo | (hi << 16);
+      }
+    }
+    return w;
+  };
+  auto mfma = [](u32x4 x, u32x4 y, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                   __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+  };
+
+  for (int L = blockIdx.x * (kThreads / kWave) + wave; L < total;
+       L += gridDim.x * (kThreads / kWave)) {
+    const int gm = L / NT, nt = L % NT;
+    const int e = find_expert(pre, a.E, gm);
+    const int mt = gm - pre[e];
+    const int row0 = a.offsets[e] + mt * G_BM;
+    const int rows_valid = min(G_BM, a.counts[e] - mt * G_BM);
+    const uint16_t* we = Bb + static_cast<int64_t>(e) * Nb * Kd;
+    const uint16_t *tp[2], *gp[2], *up[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lr + 16 * h;
+      const int src = r < rows_valid ? (a.gather ? a.gather[row0 + r] : row0 + r) : -1;
+      tp[h] = src >= 0 ? Ab + static_cast<int64_t>(src) * Kd : nullptr;
+      const int col = nt * G_BN + lr + 16 * h;
+      gp[h] = col < a.Nc ? we + static_cast<int64_t>(col) * Kd : nullptr;
+      up[h] = (kSwiglu && col < a.Nc) ? we + static_cast<int64_t>(I + col) * Kd : nullptr;
+    }
+    floatx4 accg[2][2], accu[2][2];   // [column half][token half]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) accg[i][j] = accu[i][j] = floatx4{0, 0, 0, 0};
+    constexpr int kSteps = 4;
+    for (int k0 = 0; k0 < Kd; k0 += kSteps * 32) {
+      u32x4 tv[kSteps][2], gv[kSteps][2], uv[kSteps][2];
+#pragma unroll
+      for (int c = 0; c < kSteps; ++c) {
+        const int k = k0 + c * 32 + 8 * lq;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          tv[c][h] = load8(tp[h], k);
+          gv[c][h] = load8(gp[h], k);
+          if (kSwiglu) uv[c][h] = load8(up[h], k);
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < kSteps; ++c)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            accg[i][j] = mfma(gv[c][i], tv[c][j], accg[i][j]);
+            if (kSwiglu) accu[i][j] = mfma(uv[c][i], tv[c][j], accu[i][j]);
+          }
+    }
+    // lane (lr, lq) of block [i][j]: token row 16 j + lr, output columns
+    // nt * 32 + 16 i + 4 lq + 0..3
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int r = 16 * j + lr;
+      if (r >= rows_valid) continue;
+      const int slot = a.dst ? a.dst[row0 + r] : -1;
+      const float wt = (slot >= 0 && a.wts) ? a.wts[slot] : 1.0f;
+      uint16_t* orow = slot >= 0 ? Yb + static_cast<int64_t>(slot / a.K) * a.Nc
+                                 : Cb + static_cast<int64_t>(row0 + r) * a.Nc;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int col = nt * G_BN + 16 * i + 4 * lq;
+        uint32_t v[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          float x0 = kSwiglu ? silu_mul(accg[i][j][2 * q], accu[i][j][2 * q]) : accg[i][j][2 * q];
+          float x1 = kSwiglu ? silu_mul(accg[i][j][2 * q + 1], accu[i][j][2 * q + 1])
+                             : accg[i][j][2 * q + 1];
+          uint32_t b = pack_bf16x2_hw(x0, x1);
+          if (slot >= 0)
+            b = pack_bf16x2_hw(__builtin_fmaf(wt, __uint_as_float(b << 16), 0.0f),
+                               __builtin_fmaf(wt, __uint_as_float(b & 0xffff0000u), 0.0f));
+          v[q] = b;
+        }
+        if (col + 4 <= a.Nc && (a.Nc & 3) == 0) {
+          *reinterpret_cast<uint2*>(orow + col) = uint2{v[0], v[1]};
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (col + q < a.Nc) orow[col + q] = static_cast<uint16_t>(v[q >> 1] >> (16 * (q & 1)));
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 bool gemm_can_gather(const tr_moe_desc& d) {
@@ -1327,6 +1469,25 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     }
     if (down) {
       hipLaunchKernelGGL(gemm_f32<false>, dim3(grid2), dim3(kThreads), 0, st, g2, I);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    return hipSuccess;
+  }
+
+  // bf16 shapes whose output columns do not fill the tiled kernel's tiles:
+  // the any-shape kernel for both GEMMs, one 32 x 32 tile per wave
+  if (d.H % kColMultiple || d.I % (kColMultiple / 2)) {
+    const int64_t tiles1 = (cdiv(p.R_cap, G_BM) + E) * cdiv(I, G_BN);
+    const int64_t tiles2 = (cdiv(p.R_cap, G_BM) + E) * cdiv(d.H, G_BN);
+    const int64_t b1 = cdiv(tiles1, kThreads / kWave), b2 = cdiv(tiles2, kThreads / kWave);
+    const unsigned grid1 = static_cast<unsigned>(b1 < cus * 8 ? b1 : cus * 8);
+    const unsigned grid2 = static_cast<unsigned>(b2 < cus * 8 ? b2 : cus * 8);
+    if (up) {
+      hipLaunchKernelGGL(gemm_any<true>, dim3(grid1), dim3(kThreads), 0, st, g1, I);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (down) {
+      hipLaunchKernelGGL(gemm_any<false>, dim3(grid2), dim3(kThreads), 0, st, g2, I);
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     return hipSuccess;

@@ -15,7 +15,8 @@ constexpr int kStreamMaxRows = 32;
 // Spare rows after R_cap in the expanded (Xe) and intermediate (h) buffers,
 // so GEMM tiles may read a full tile of rows from any segment start.
 constexpr int kRowPad = 256;
-// bf16 shapes: H a multiple of kColMultiple, I of kColMultiple / 2.
+// bf16 shapes of the tiled and streaming GEMM kernels: H a multiple of
+// kColMultiple, I of kColMultiple / 2 (other shapes: the any-shape kernel).
 constexpr int kColMultiple = 256;
 // Most worker blocks of a DP-padded buffer (their counts' prefix sits in LDS).
 constexpr int kMaxPadBlocks = 4096;
