@@ -103,6 +103,14 @@ def test_padded_route_edge_cases():
     # 64 experts over ~254 scan blocks (batched partial sums)
     T, B = 20000, 96
     _check_route(rng.integers(-1, 64, size=(T, 8)), 64, B, rng.integers(0, B + 1, size=-(-T // B)))
+    # small batches (the single-block kernel, T * K <= 1024): padding blocks
+    # with counts below 0, inside and above the block, rows straddling waves
+    T, B = 200, 16
+    _check_route(rng.integers(-1, 10, size=(T, 4)), 10, B, rng.integers(-3, B + 4, size=-(-T // B)))
+    T, B = 341, 5
+    _check_route(rng.integers(-1, 7, size=(T, 3)), 7, B, rng.integers(-1, B + 2, size=-(-T // B)))
+    _check_route(rng.integers(0, 3, size=(20, 8)), 3, 4, np.array([4, 0, 2, 9, 1], np.int32),
+                 flags=tr.FLAG_GEMM_FORCE_TILED)
     # the GEMM modes' expert counts (experts with 1..32 and with more routes)
     T, B = 3000, 50
     idx = np.where(rng.random((T, 4)) < 0.02, rng.integers(0, 40, size=(T, 4)),

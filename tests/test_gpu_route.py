@@ -15,11 +15,14 @@ from tests._gpu import say
 pytestmark = pytest.mark.gpu
 
 
-def _check(idx_np, E, eb=0, idx_dtype=torch.int64, H=256, I=128):
+def _check(idx_np, E, eb=0, idx_dtype=torch.int64, H=256, I=128, flags=0):
     T, K = idx_np.shape
-    say(f"route T={T} K={K} E={E} eb={eb} idx={idx_dtype}")
+    say(f"route T={T} K={K} E={E} eb={eb} idx={idx_dtype} flags={flags}")
     idx = torch.from_numpy(np.ascontiguousarray(idx_np)).to(idx_dtype).cuda()
-    p = tr.plan(idx, E=E, H=H, I=I, dtype=torch.bfloat16, expert_begin=eb)
+    p = tr.plan(idx, E=E, H=H, I=I, dtype=torch.bfloat16, expert_begin=eb, flags=flags)
+    # fewest routes of an expert the tiled GEMM takes, per the plan's mode
+    lo = (1 if flags & tr.FLAG_GEMM_FORCE_TILED
+          else np.iinfo(np.int64).max if flags & tr.FLAG_GEMM_FORCE_STREAM else 33)
     stats = tr.plan_stats(p)
     v = p.views()
     ref = oracle.route(idx_np, E, eb)
@@ -30,13 +33,14 @@ def _check(idx_np, E, eb=0, idx_dtype=torch.int64, H=256, I=128):
     assert np.array_equal(v["row_src"][:R].cpu().numpy(), ref["row_src"])
     assert np.array_equal(v["row_k"][:R].cpu().numpy(), ref["row_k"])
     # row_dst by its definition from the oracle's route: the slot of a
-    # received row with exactly one local slot whose expert has more than 32
-    # routes (the tiled GEMM's experts), -1 for every other row
+    # received row with exactly one local slot whose expert the tiled GEMM
+    # takes (more than 32 routes in the automatic mode), -1 for every other
+    # row
     rm = ref["row_map"]
     n_loc = (rm >= 0).sum(1)
     want = np.full(R, -1, np.int64)
     tt, kk = np.nonzero((rm >= 0) & (n_loc[:, None] == 1))
-    tiled = ref["counts"][idx_np[tt, kk] - eb] > 32
+    tiled = ref["counts"][idx_np[tt, kk] - eb] >= lo
     tt, kk = tt[tiled], kk[tiled]
     want[rm[tt, kk]] = tt * K + kk
     assert np.array_equal(v["row_dst"][:R].cpu().numpy(), want)
@@ -48,10 +52,10 @@ def _check(idx_np, E, eb=0, idx_dtype=torch.int64, H=256, I=128):
     local = (idx_np >= eb) & (idx_np < eb + E)
     assert stats == (R, int(local.any(1).sum()) if T else 0, int((~local).sum()),
                      int((ref["counts"] == 0).sum()))
-    # experts of the streaming GEMM (1..32 routes) and of the tiled GEMM (> 32)
+    # experts of the streaming GEMM and of the tiled GEMM
     c = ref["counts"]
-    assert int(v["stats"][6]) == int(((c > 0) & (c <= 32)).sum())
-    assert int(v["stats"][7]) == int((c > 32).sum())
+    assert int(v["stats"][6]) == int(((c > 0) & (c < lo)).sum())
+    assert int(v["stats"][7]) == int((c >= lo).sum())
 
 
 @pytest.mark.parametrize("name,T", [("c1", None), ("c2", None), ("c3", 1), ("c3", 8), ("c3", 64),
@@ -85,6 +89,27 @@ def test_route_edge_cases():
     _check(rng.integers(-1, 64, size=(20000, 8)), 64)
     _check(rng.integers(-1, 256, size=(30000, 8)), 256)
     _check(rng.integers(-1, 48, size=(40000, 32)), 48)
+
+
+def test_route_small_batches():
+    """The single-block kernel of T * K <= 1024 slots (decode batches): every
+    expert count up to 1024, K = 1 .. 32, rows straddling waves (K = 3),
+    one hot expert, and the GEMM modes."""
+    rng = np.random.default_rng(6)
+    _check(rng.integers(-1, 1024, size=(32, 32)), 1024)            # max slots, max E
+    _check(rng.integers(-2, 12, size=(341, 3)), 10)                # K = 3, 1023 slots
+    _check(np.zeros((1, 1), np.int64), 1)                          # one slot
+    _check(np.full((64, 16), 3, np.int64), 4)                      # one expert, 16 per row
+    _check(rng.integers(0, 5, size=(1024, 1)), 5)                  # single-slot rows, tiled
+    _check(rng.integers(-1, 40, size=(3, 7)), 40, idx_dtype=torch.int32)
+    g = rng.integers(-1, 64, size=(100, 8))
+    _check(np.where(g >= 0, g + 100, -1), 16, eb=108)             # expert_begin, foreign ids
+    for fl in (tr.FLAG_GEMM_FORCE_TILED, tr.FLAG_GEMM_FORCE_STREAM):
+        _check(rng.integers(-1, 6, size=(200, 4)), 6, flags=fl)
+        _check(rng.integers(-1, 40, size=(1000, 1)), 40, flags=fl)
+    # just past the single-block kernel: a few blocks of the general kernels
+    _check(rng.integers(-1, 40, size=(1025, 1)), 40)
+    _check(rng.integers(-1, 28, size=(256, 16)), 28)
 
 
 def test_route_deterministic():

@@ -23,8 +23,9 @@
 //    the rows without exactly one local slot and, per expert, the rows whose
 //    one local slot goes to it, so each block's first entry follows from the
 //    same partial sums once the experts' totals are known.
-//  - a small input (T*K <= 4096) runs as one block that counts for itself:
-//    one launch instead of two.
+//  - a small input runs as one block: up to 1024 slots a single-block
+//    kernel with one slot per thread (decode batches), up to 2048 the
+//    general scatter counting for itself; one launch instead of two.
 //  - a DP-padded buffer (SGLang PR #6092: workers' batches padded to one
 //    shape) names per block of rows how many carry tokens; the other rows are
 //    treated as rows without a local slot, and their ids are never loaded.
@@ -491,6 +492,165 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
   }
 }
 
+
+// Small inputs (T * K <= kSmallSlots: decode batches): one block of
+// kSmallSlots threads, one slot per thread and, for the row phase, one row per
+// thread. Every global load (the slot's id, the rows' block counts) goes out
+// at the start; the rest runs in LDS between block barriers:
+//   0. the slot's local expert (E: none) into se[];
+//   1. ranks among the wave's slots of the same expert (ids matched bit by
+//      bit with ballots); each (wave, expert) leader stores its count;
+//   2. per expert: its count in each earlier wave (an exclusive prefix over
+//      the 16 waves), its total, and the segment offsets (one block scan);
+//   3. each local slot's row: offset + earlier waves' count + rank;
+//   4. per received row: the fused GEMM2 destination of a row with exactly
+//      one local slot of a tiled expert, and tok_rest in row order (a second
+//      block scan).
+// Same results, bit for bit, as the general kernels.
+constexpr int kSmallSlots = 1024;
+constexpr int kSmallWaves = kSmallSlots / kWave;
+
+template <typename IdxT>
+__global__ __launch_bounds__(kSmallSlots) void route_small(
+    const IdxT* __restrict__ idx, int T, int K, int64_t eb, int E, int B,
+    const int* __restrict__ bc, int* __restrict__ counts, int* __restrict__ offsets,
+    int* __restrict__ row_map, int* __restrict__ row_src, int* __restrict__ row_k,
+    int* __restrict__ stats, int* __restrict__ row_dst, int* __restrict__ tok_rest,
+    int min_tiled) {
+  __shared__ int cw[kSmallWaves * kMaxE];   // [wave][E] counts, then earlier waves' counts
+  __shared__ int tot[kMaxE];                // routes per expert
+  __shared__ int off[kMaxE];                // segment starts
+  __shared__ int se[kSmallSlots];           // slot's local expert (E: none)
+  __shared__ int sr[kSmallSlots];           // slot's expanded row (-1: none)
+  __shared__ int tmp[kSmallWaves];
+  // [0] ignored slots, [1] rows with a local slot, [2] carrying rows,
+  // [3] empty experts, [4] / [5] experts of the streaming / tiled GEMM
+  __shared__ int misc[6];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int TK = T * K;                     // <= kSmallSlots
+  const int s = tid;                        // this thread's slot
+  const int ts = s / K;                     // its received row
+
+  // 0. the loads: the slot's id (clamped, so that it goes out at once) and,
+  // for a padded plan, the block counts of the slot's row and of row tid;
+  // a padding row's ids are never read
+  IdxT id = 0;
+  int bcs = 1, bct = 1;
+  if (TK > 0) {
+    if (B == 0) {
+      id = idx[s < TK ? s : TK - 1];
+    } else {
+      bcs = bc[min(ts, T - 1) / B];
+      bct = bc[min(tid, T - 1) / B];
+    }
+  }
+  for (int i = tid; i < kSmallWaves * E; i += kSmallSlots) cw[i] = 0;
+  if (tid < 6) misc[tid] = 0;
+  const bool carry_s = s < TK && (B == 0 || ts - ts / B * B < bcs);
+  if (B > 0 && carry_s) id = idx[s];
+  const int e = carry_s ? local_of(id, eb, E) : E;
+  const bool valid = e < E;
+  se[s] = e;
+  __syncthreads();
+
+  // 1. rank among the wave's slots of the same expert
+  const int nbits = 32 - __clz(E);          // bits of the values 0..E
+  uint64_t peers = __ballot(1);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    peers &= bit ? bal : ~bal;
+  }
+  const int rank = popc_below(peers);
+  if (valid && rank == 0) cw[wave * E + e] = __popcll(peers);
+  const uint64_t ign = __ballot(carry_s && !valid);
+  if (lane_id() == 0 && ign) atomicAdd(&misc[0], __popcll(ign));
+  __syncthreads();
+
+  // 2. per expert (thread tid = e): earlier waves' counts, total, offsets
+  int te = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) {
+      const int c = cw[w * E + tid];
+      cw[w * E + tid] = te;
+      te += c;
+    }
+  }
+  int R = 0;
+  const int o = block_exclusive_scan<kSmallSlots>(tid < E ? te : 0, tmp, &R);
+  if (tid < E) {
+    tot[tid] = te;
+    off[tid] = o;
+    counts[tid] = te;
+    offsets[tid] = o;
+  }
+  if (tid == 0) offsets[E] = R;
+  const uint64_t emp = __ballot(tid < E && te == 0);
+  const uint64_t str = __ballot(tid < E && te > 0 && te < min_tiled);
+  const uint64_t til = __ballot(tid < E && te >= min_tiled);
+  if (lane_id() == 0) {
+    if (emp) atomicAdd(&misc[3], __popcll(emp));
+    if (str) atomicAdd(&misc[4], __popcll(str));
+    if (til) atomicAdd(&misc[5], __popcll(til));
+  }
+  __syncthreads();
+
+  // 3. the slot's row
+  const int row = valid ? off[e] + cw[wave * E + e] + rank : -1;
+  if (s < TK) {
+    row_map[s] = row;
+    if (valid) {
+      row_src[row] = ts;
+      row_k[row] = s - ts * K;
+    }
+  }
+  sr[s] = row;
+  __syncthreads();
+
+  // 4. row tid: fused destination, tok_rest
+  bool rest = false;
+  int n = 0;
+  if (tid < T) {
+    int e1 = E;
+    const int* re = se + tid * K;
+    const int* rr = sr + tid * K;
+    for (int k = 0; k < K; ++k) {
+      if (rr[k] >= 0) {
+        ++n;
+        e1 = re[k];
+      }
+    }
+    const bool direct = n == 1 && tot[e1] >= min_tiled;
+    for (int k = 0; k < K; ++k) {
+      const int m = rr[k];
+      if (m >= 0) row_dst[m] = direct ? tid * K + k : -1;
+    }
+    rest = !direct;
+  }
+  const uint64_t loc = __ballot(n > 0);
+  const uint64_t car = __ballot(tid < T && (B == 0 || tid - tid / B * B < bct));
+  if (lane_id() == 0) {
+    if (loc) atomicAdd(&misc[1], __popcll(loc));
+    if (car) atomicAdd(&misc[2], __popcll(car));
+  }
+  int n_rest = 0;
+  const int pos = block_exclusive_scan<kSmallSlots>(rest ? 1 : 0, tmp, &n_rest);
+  if (rest) tok_rest[pos] = tid;
+  if (tid == 0) {
+    stats[0] = R;
+    stats[1] = misc[1];
+    stats[2] = misc[0];
+    stats[3] = misc[3];
+    stats[4] = n_rest;
+    stats[5] = misc[2];
+    stats[6] = misc[4];
+    stats[7] = misc[5];
+  }
+}
+
 template <typename IdxT>
 hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
   const tr_moe_desc& d = p.d;
@@ -503,6 +663,12 @@ hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
   // fewest routes of an expert the grouped GEMM tiles (the others stream)
   const int min_tiled = (d.flags & TR_FLAG_GEMM_FORCE_STREAM) ? INT32_MAX
                         : (d.flags & TR_FLAG_GEMM_FORCE_TILED) ? 1 : kStreamMaxRows + 1;
+  if (d.T * K <= kSmallSlots) {
+    hipLaunchKernelGGL((route_small<IdxT>), dim3(1), dim3(kSmallSlots), 0, st, idx,
+                       static_cast<int>(d.T), K, d.expert_begin, E, B, bc, p.counts, p.offsets,
+                       p.row_map, p.row_src, p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
+    return hipGetLastError();
+  }
   if (nb == 1) {
     hipLaunchKernelGGL((route_scatter<IdxT, true>), dim3(1), dim3(kThreads), sh_scatter, st, idx,
                        d.T, K, d.expert_begin, E, rpb, nb, B, bc, p.scan_tmp, p.counts, p.offsets,
@@ -527,10 +693,12 @@ hipError_t route_scan(const tr_moe_plan& p, const void* idx, hipStream_t st) {
 }
 
 void route_scan_geometry(int64_t T, int K, int* blocks, int* rows_per_block) {
-  // One block for small inputs; otherwise ~512 slots per block (two ranking
-  // rounds: the blocks are latency-bound, so more and shorter ones), at most
-  // kMaxScanBlocks blocks.
-  if (T * K <= 4096) {
+  // One block for small inputs (up to kSmallSlots slots the single-block
+  // kernel, up to 2048 the general one counting for itself: measured faster
+  // than several blocks there, slower at 4096); otherwise ~512 slots per
+  // block (two ranking rounds: the blocks are latency-bound, so more and
+  // shorter ones), at most kMaxScanBlocks blocks.
+  if (T * K <= 2048) {
     *blocks = 1;
     *rows_per_block = static_cast<int>(T > 0 ? T : 1);
     return;
