@@ -690,12 +690,14 @@ __device__ __forceinline__ void gemm_tiles_impl(const GemmArgs& a, int I, const 
     // nothing
     uint16_t* drow[4];
     bool to_y[4], rvalid[4];
+    float yadd[4];
     if (fused) {
       uint16_t* __restrict__ Yb = static_cast<uint16_t*>(a.y);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int lrow = wm * 128 + i * 32 + (lane & 31);
         to_y[i] = slot_c[i] >= 0;
+        yadd[i] = to_y[i] ? 0.0f : -0.0f;
         rvalid[i] = lrow < t.rows_valid;
         drow[i] = to_y[i] ? Yb + static_cast<int64_t>(slot_c[i] / a.K) * a.Nc
                           : Cb + static_cast<int64_t>(t.row0 + lrow) * a.Nc;
@@ -749,15 +751,17 @@ __device__ __forceinline__ void gemm_tiles_impl(const GemmArgs& a, int I, const 
             // as the reduce writes it: fma(w, bf16 output, +0) in fp32,
             // rounded once (the +0 start of the reduce's sum decides the sign
             // of zero); the other rows go to O. One store either way, through
-            // a per-lane address; rows past the segment store nothing.
-            u32x4 v = out;
+            // a per-lane address; rows past the segment store nothing. A row
+            // to O takes the same arithmetic with w = 1 and the addend -0,
+            // which returns its bf16 value unchanged (fma(1, v, -0) = v for
+            // every v, zeros of both signs included), so there is no select
+            // per value.
+            u32x4 v;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t yv =
-                  pack_bf16x2_hw(__builtin_fmaf(ywt[i], __uint_as_float(out[e] << 16), 0.0f),
-                                 __builtin_fmaf(ywt[i], __uint_as_float(out[e] & 0xffff0000u), 0.0f));
-              v[e] = to_y[i] ? yv : out[e];
-            }
+            for (int e = 0; e < 4; ++e)
+              v[e] = pack_bf16x2_hw(
+                  __builtin_fmaf(ywt[i], __uint_as_float(out[e] << 16), yadd[i]),
+                  __builtin_fmaf(ywt[i], __uint_as_float(out[e] & 0xffff0000u), yadd[i]));
             if (rvalid[i]) *reinterpret_cast<u32x4*>(drow[i] + col) = v;
           }
         }
