@@ -97,6 +97,10 @@ def test_route_small_batches():
     one hot expert, and the GEMM modes."""
     rng = np.random.default_rng(6)
     _check(rng.integers(-1, 1024, size=(32, 32)), 1024)            # max slots, max E
+    _check(rng.integers(-1, 1024, size=(2, 32)), 1024)             # 64 slots: one wave, 16 experts a thread
+    _check(rng.integers(-1, 1024, size=(8, 32)), 1024)             # 256 slots: four waves
+    _check(rng.integers(-1, 3, size=(60, 1)), 3)
+    _check(rng.integers(-1, 20, size=(13, 5)), 17)                 # 65 slots
     _check(rng.integers(-2, 12, size=(341, 3)), 10)                # K = 3, 1023 slots
     _check(np.zeros((1, 1), np.int64), 1)                          # one slot
     _check(np.full((64, 16), 3, np.int64), 4)                      # one expert, 16 per row

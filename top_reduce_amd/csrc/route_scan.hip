@@ -493,43 +493,46 @@ __global__ __launch_bounds__(kThreads) void route_scatter(
 }
 
 
-// Small inputs (T * K <= kSmallSlots: decode batches): one block of
-// kSmallSlots threads, one slot per thread and, for the row phase, one row per
-// thread. Every global load (the slot's id, the rows' block counts) goes out
-// at the start; the rest runs in LDS between block barriers:
+// Small inputs (T * K <= kSmallSlots: decode batches): one block of kSlots
+// threads (64, 256 or 1024, the fewest that hold every slot), one slot per
+// thread and, for the row phase, one row per thread. Every global load (the
+// slot's id, the rows' block counts) goes out at the start; the rest runs in
+// LDS between block barriers:
 //   0. the slot's local expert (E: none) into se[];
 //   1. ranks among the wave's slots of the same expert (ids matched bit by
 //      bit with ballots); each (wave, expert) leader stores its count;
-//   2. per expert: its count in each earlier wave (an exclusive prefix over
-//      the 16 waves), its total, and the segment offsets (one block scan);
+//   2. per expert (a run of experts per thread): its count in each earlier
+//      wave (an exclusive prefix over the waves), its total, and the segment
+//      offsets (one block scan);
 //   3. each local slot's row: offset + earlier waves' count + rank;
 //   4. per received row: the fused GEMM2 destination of a row with exactly
 //      one local slot of a tiled expert, and tok_rest in row order (a second
 //      block scan).
 // Same results, bit for bit, as the general kernels.
 constexpr int kSmallSlots = 1024;
-constexpr int kSmallWaves = kSmallSlots / kWave;
 
-template <typename IdxT>
-__global__ __launch_bounds__(kSmallSlots) void route_small(
+template <typename IdxT, int kSlots>
+__global__ __launch_bounds__(kSlots) void route_small(
     const IdxT* __restrict__ idx, int T, int K, int64_t eb, int E, int B,
     const int* __restrict__ bc, int* __restrict__ counts, int* __restrict__ offsets,
     int* __restrict__ row_map, int* __restrict__ row_src, int* __restrict__ row_k,
     int* __restrict__ stats, int* __restrict__ row_dst, int* __restrict__ tok_rest,
     int min_tiled) {
-  __shared__ int cw[kSmallWaves * kMaxE];   // [wave][E] counts, then earlier waves' counts
+  constexpr int kW = kSlots / kWave;
+  constexpr int kPerE = kMaxE / kSlots;     // most experts per thread
+  __shared__ int cw[kW * kMaxE];            // [wave][E] counts, then earlier waves' counts
   __shared__ int tot[kMaxE];                // routes per expert
   __shared__ int off[kMaxE];                // segment starts
-  __shared__ int se[kSmallSlots];           // slot's local expert (E: none)
-  __shared__ int sr[kSmallSlots];           // slot's expanded row (-1: none)
-  __shared__ int tmp[kSmallWaves];
+  __shared__ int se[kSlots];                // slot's local expert (E: none)
+  __shared__ int sr[kSlots];                // slot's expanded row (-1: none)
+  __shared__ int tmp[kW];
   // [0] ignored slots, [1] rows with a local slot, [2] carrying rows,
   // [3] empty experts, [4] / [5] experts of the streaming / tiled GEMM
   __shared__ int misc[6];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
-  const int TK = T * K;                     // <= kSmallSlots
+  const int TK = T * K;                     // <= kSlots
   const int s = tid;                        // this thread's slot
   const int ts = s / K;                     // its received row
 
@@ -546,7 +549,7 @@ __global__ __launch_bounds__(kSmallSlots) void route_small(
       bct = bc[min(tid, T - 1) / B];
     }
   }
-  for (int i = tid; i < kSmallWaves * E; i += kSmallSlots) cw[i] = 0;
+  for (int i = tid; i < kW * E; i += kSlots) cw[i] = 0;
   if (tid < 6) misc[tid] = 0;
   const bool carry_s = s < TK && (B == 0 || ts - ts / B * B < bcs);
   if (B > 0 && carry_s) id = idx[s];
@@ -569,32 +572,50 @@ __global__ __launch_bounds__(kSmallSlots) void route_small(
   if (lane_id() == 0 && ign) atomicAdd(&misc[0], __popcll(ign));
   __syncthreads();
 
-  // 2. per expert (thread tid = e): earlier waves' counts, total, offsets
-  int te = 0;
-  if (tid < E) {
+  // 2. per expert (experts tid * per .. + per - 1): earlier waves' counts,
+  // totals, offsets
+  const int per = (E + kSlots - 1) / kSlots;
+  int te[kPerE];
+  int sum = 0;
 #pragma unroll
-    for (int w = 0; w < kSmallWaves; ++w) {
-      const int c = cw[w * E + tid];
-      cw[w * E + tid] = te;
-      te += c;
+  for (int j = 0; j < kPerE; ++j) {
+    te[j] = 0;
+    const int x = tid * per + j;
+    if (j < per && x < E) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        const int c = cw[w * E + x];
+        cw[w * E + x] = te[j];
+        te[j] += c;
+      }
+      sum += te[j];
     }
   }
   int R = 0;
-  const int o = block_exclusive_scan<kSmallSlots>(tid < E ? te : 0, tmp, &R);
-  if (tid < E) {
-    tot[tid] = te;
-    off[tid] = o;
-    counts[tid] = te;
-    offsets[tid] = o;
+  int o = block_exclusive_scan<kSlots>(sum, tmp, &R);
+  int n_emp = 0, n_str = 0, n_til = 0;
+#pragma unroll
+  for (int j = 0; j < kPerE; ++j) {
+    const int x = tid * per + j;
+    if (j < per && x < E) {
+      tot[x] = te[j];
+      off[x] = o;
+      counts[x] = te[j];
+      offsets[x] = o;
+      o += te[j];
+      n_emp += te[j] == 0;
+      n_str += te[j] > 0 && te[j] < min_tiled;
+      n_til += te[j] >= min_tiled;
+    }
   }
   if (tid == 0) offsets[E] = R;
-  const uint64_t emp = __ballot(tid < E && te == 0);
-  const uint64_t str = __ballot(tid < E && te > 0 && te < min_tiled);
-  const uint64_t til = __ballot(tid < E && te >= min_tiled);
+  n_emp = wave_sum(n_emp);
+  n_str = wave_sum(n_str);
+  n_til = wave_sum(n_til);
   if (lane_id() == 0) {
-    if (emp) atomicAdd(&misc[3], __popcll(emp));
-    if (str) atomicAdd(&misc[4], __popcll(str));
-    if (til) atomicAdd(&misc[5], __popcll(til));
+    if (n_emp) atomicAdd(&misc[3], n_emp);
+    if (n_str) atomicAdd(&misc[4], n_str);
+    if (n_til) atomicAdd(&misc[5], n_til);
   }
   __syncthreads();
 
@@ -637,7 +658,7 @@ __global__ __launch_bounds__(kSmallSlots) void route_small(
     if (car) atomicAdd(&misc[2], __popcll(car));
   }
   int n_rest = 0;
-  const int pos = block_exclusive_scan<kSmallSlots>(rest ? 1 : 0, tmp, &n_rest);
+  const int pos = block_exclusive_scan<kSlots>(rest ? 1 : 0, tmp, &n_rest);
   if (rest) tok_rest[pos] = tid;
   if (tid == 0) {
     stats[0] = R;
@@ -664,9 +685,19 @@ hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
   const int min_tiled = (d.flags & TR_FLAG_GEMM_FORCE_STREAM) ? INT32_MAX
                         : (d.flags & TR_FLAG_GEMM_FORCE_TILED) ? 1 : kStreamMaxRows + 1;
   if (d.T * K <= kSmallSlots) {
-    hipLaunchKernelGGL((route_small<IdxT>), dim3(1), dim3(kSmallSlots), 0, st, idx,
-                       static_cast<int>(d.T), K, d.expert_begin, E, B, bc, p.counts, p.offsets,
-                       p.row_map, p.row_src, p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
+    const int T = static_cast<int>(d.T), TK = T * K;
+    if (TK <= 64)
+      hipLaunchKernelGGL((route_small<IdxT, 64>), dim3(1), dim3(64), 0, st, idx, T, K,
+                         d.expert_begin, E, B, bc, p.counts, p.offsets, p.row_map, p.row_src,
+                         p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
+    else if (TK <= 256)
+      hipLaunchKernelGGL((route_small<IdxT, 256>), dim3(1), dim3(256), 0, st, idx, T, K,
+                         d.expert_begin, E, B, bc, p.counts, p.offsets, p.row_map, p.row_src,
+                         p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
+    else
+      hipLaunchKernelGGL((route_small<IdxT, kSmallSlots>), dim3(1), dim3(kSmallSlots), 0, st,
+                         idx, T, K, d.expert_begin, E, B, bc, p.counts, p.offsets, p.row_map,
+                         p.row_src, p.row_k, p.stats, p.row_dst, p.tok_rest, min_tiled);
     return hipGetLastError();
   }
   if (nb == 1) {
