@@ -286,6 +286,37 @@ def test_forward_fused_equals_stages(name, flags, T):
         assert torch.equal(y_3.view(torch.int16), y_s.view(torch.int16)), "fused stages != stages"
 
 
+# decode batches (at most 32 expanded rows): the forward runs the reduce
+# inside GEMM2; one local expert, several, every slot local (dense), K = 8
+gen.custom_spec("decode_k8", T=4, K=8, E=12, G=24, H=512, I=256, zipf_s=0.3, seed=16)
+
+
+@pytest.mark.parametrize("name,T,variant", [("c3", 1, ""), ("c3", 2, ""), ("c3", 1, "random"),
+                                            ("c3", 2, "random"), ("c3", 2, "dense"),
+                                            ("decode_k8", None, "")])
+def test_decode_forward_equals_stages(name, T, variant):
+    """A decode forward (GEMM2 with the reduce folded in) equals the unfused
+    composition expand -> grouped GEMM -> reduce bit for bit, with and without
+    weights, NaN in the non-local weights included."""
+    say(f"decode forward {name} T={T} {variant}")
+    wl = gen.make_workload(name, T=T, variant=variant, with_weights=True)
+    assert wl.T * wl.K <= 32
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch_dtype(wl))
+    wn = wl.weights.copy()
+    wn[~((wl.idx >= 0) & (wl.idx < wl.E))] = np.nan
+    for w in (d["w"], None, dev(wn)):
+        y_f = tr.forward(p, d["x"], w, d["w1"], d["w2"])
+        tr.expand(p, d["x"])
+        tr.grouped_gemm(p, d["w1"], d["w2"])
+        y_s = tr.combine_reduce(p, w)
+        torch.cuda.synchronize()
+        assert torch.equal(y_f.view(torch.int16), y_s.view(torch.int16)), "forward != stages"
+    ref = oracle.forward(wl.x, wl.idx, wl.weights, wl.w1, wl.w2, wl.E)
+    y = host(tr.forward(p, d["x"], d["w"], d["w1"], d["w2"]))
+    _assert_close(as_f64(y), ref, wl.dtype, f"{name} decode y")
+
+
 @pytest.mark.parametrize("name,flags,T", [("mid", 0, None), ("mid", tr.FLAG_GEMM_FORCE_TILED, None),
                                           ("mid", tr.FLAG_GEMM_FORCE_STREAM, None),
                                           ("mid_small_experts", 0, None), ("c3", 0, 1)])

@@ -361,10 +361,12 @@ tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_
     // GEMM1 reads x through the route table (no expand pass, Xe unused);
     // GEMM2 writes received rows with one local slot straight to y, and the
     // reduce completes the others
+    bool y_done = false;
     if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream, x,
-                                         topk_weights, y),
+                                         topk_weights, y, &y_done),
                         "moe_grouped_gemm launch")) != TR_OK)
       return s;
+    if (y_done) return ok();   // a decode batch: GEMM2 ran the reduce
     return hip_status(tr::combine_reduce(*plan, nullptr, topk_weights, y, stream, true),
                       "moe_combine_reduce launch");
   } else {

@@ -1187,6 +1187,143 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode(GemmArgs a, int I) {
   }
 }
 
+
+// Decode GEMM2 with the weighted top-k reduce folded in (moe_forward on a
+// decode batch: at most kStreamMaxRows expanded rows, so at most that many
+// received rows and slots). One unit is 16 output columns of every row: the
+// block computes them for each active expert in turn, exactly as gemm_decode
+// does (same split of k over the waves, same fixed-order sum, the same bf16
+// rounding of O), keeps the rounded values in LDS, and then sums each
+// received row's local slots in slot order into y, as fma(w, o, acc) from
+// +0 and rounded once, exactly as the reduce kernel does. No row of O goes to
+// memory and the reduce needs no launch of its own; a received row with no
+// local slot gets +0. Rows at or past n_rows count as absent, as in the
+// reduce; a slot's weight is read only when the slot is local.
+template <int kDecB>
+__global__ __launch_bounds__(kDecThreads) void gemm_decode_y(GemmArgs a,
+                                                             const int* __restrict__ row_map,
+                                                             int64_t n_rows) {
+  __shared__ int pre[kMaxE + 1];
+  __shared__ int list[kMaxE];
+  __shared__ int cnt_s[kMaxE], off_s[kMaxE];
+  __shared__ int tmp[kDecWaves];
+  __shared__ floatx4 red[kDecWaves][kWave];
+  __shared__ uint32_t o_s[kStreamMaxRows][8];   // bf16 pairs: row r, columns 2 i, 2 i + 1
+  __shared__ int map_s[kStreamMaxRows];
+  __shared__ float w_s[kStreamMaxRows];
+
+  const int tid = threadIdx.x;
+  const int TK = static_cast<int>(a.T) * a.K;   // <= kStreamMaxRows
+  int offv[kMaxE / kDecThreads], cntv[kMaxE / kDecThreads];
+#pragma unroll
+  for (int j = 0; j < kMaxE / kDecThreads; ++j) {
+    const int e = min(tid + j * kDecThreads, a.E - 1);
+    offv[j] = j * kDecThreads < a.E ? a.offsets[e] : 0;
+    cntv[j] = j * kDecThreads < a.E ? a.counts[e] : 0;
+  }
+  int mv = -1;
+  if (tid < TK) {
+    mv = row_map[tid];
+    if (mv >= n_rows) mv = -1;
+  }
+  const int mode = a.mode;
+  const int n_elig = expert_prefix<kDecThreads>(a.counts, a.E, [mode](int c) {
+    return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
+  }, pre, tmp);
+#pragma unroll
+  for (int j = 0; j < kMaxE / kDecThreads; ++j) {
+    const int e = tid + j * kDecThreads;
+    if (e < a.E) {
+      if (pre[e + 1] > pre[e]) list[pre[e]] = e;
+      cnt_s[e] = cntv[j];
+      off_s[e] = offv[j];
+    }
+  }
+  if (tid < TK) map_s[tid] = mv;
+  // the local slots' weights: needed only after the first unit's MFMAs
+  const float wv = (tid < TK && mv >= 0 && a.wts) ? a.wts[tid] : 1.0f;
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 4;                         // k group of the lane
+  const int arow = lane & 15;                      // operand row of the lane
+  const int Kd = a.Kd;
+  const int nk32 = Kd / 32;
+  const int kb0 = wave * nk32 / kDecWaves, kb1 = (wave + 1) * nk32 / kDecWaves;
+  const int64_t Nb = a.Nc;
+  const uint16_t* __restrict__ Ab = static_cast<const uint16_t*>(a.A);
+  const uint16_t* __restrict__ Bb = static_cast<const uint16_t*>(a.B);
+  uint16_t* __restrict__ Yb = static_cast<uint16_t*>(a.y);
+  const int n_units = (a.Nc + 15) / 16;
+  bool w_stored = false;
+
+  for (int c = blockIdx.x; c < n_units; c += gridDim.x) {
+    const int64_t wrow = min(c * 16 + arow, a.Nc - 1);
+    for (int q = 0; q < n_elig; ++q) {
+      const int e = list[q];
+      const int cnt = cnt_s[e];
+      const int off = off_s[e];
+      const uint16_t* wp = Bb + (static_cast<int64_t>(e) * Nb + wrow) * Kd + g * 8;
+      for (int tb = 0; tb < cnt; tb += 16) {
+        const int tok = tb + arow;
+        const bool xv = tok < cnt;
+        const int r = off + (xv ? tok : 0);
+        floatx4 acc = {0, 0, 0, 0};
+        for (int kb = kb0; kb < kb1; kb += kDecB) {
+          u32x4 wa[kDecB], xb[kDecB];
+#pragma unroll
+          for (int j = 0; j < kDecB; ++j)
+            wa[j] = *reinterpret_cast<const u32x4*>(wp + min(kb + j, kb1 - 1) * 32);
+          const uint16_t* xp = Ab + static_cast<int64_t>(r) * Kd + g * 8;
+#pragma unroll
+          for (int j = 0; j < kDecB; ++j)
+            if (kb + j < kb1)
+              xb[j] = xv ? *reinterpret_cast<const u32x4*>(xp + (kb + j) * 32) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < kDecB; ++j)
+            if (kb + j < kb1)
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wa[j]),
+                                                            __builtin_bit_cast(bf16x8, xb[j]), acc,
+                                                            0, 0, 0);
+        }
+        red[wave][lane] = acc;
+        __syncthreads();
+        if (wave == 0 && xv) {
+          // lane (g, r): columns 4 g .. 4 g + 3 of the unit for row off + tok
+          floatx4 sum = red[0][lane];
+#pragma unroll
+          for (int w = 1; w < kDecWaves; ++w) sum += red[w][lane];
+          o_s[off + tok][2 * g] = pack_bf16x2(sum[0], sum[1]);
+          o_s[off + tok][2 * g + 1] = pack_bf16x2(sum[2], sum[3]);
+        }
+        __syncthreads();
+      }
+    }
+    if (!w_stored) {
+      if (tid < TK) w_s[tid] = wv;
+      w_stored = true;
+      __syncthreads();
+    }
+    // the reduce: thread (t, column) of the unit
+    const int t = tid >> 4, col = tid & 15;
+    if (t < a.T && c * 16 + col < a.Nc) {
+      float acc = 0.0f;
+      for (int k = 0; k < a.K; ++k) {
+        const int m = map_s[t * a.K + k];
+        if (m >= 0) {
+          const uint32_t pair = o_s[m][col >> 1];
+          acc = fmaf(w_s[t * a.K + k], bf16_bits_to_f32((col & 1) ? (pair >> 16) : (pair & 0xffffu)),
+                     acc);
+        }
+      }
+      Yb[static_cast<int64_t>(t) * a.Nc + c * 16 + col] =
+          static_cast<uint16_t>(pack_bf16x2(acc, 0.0f) & 0xffffu);
+    }
+    __syncthreads();
+  }
+}
+
 // --------------------------------------------------------------------------
 // fp32 kernel: fp32 MFMA (v_mfma_f32_16x16x4_f32), one wave per 16-row x
 // 16-output tile
@@ -1428,7 +1565,8 @@ bool gemm_can_gather(const tr_moe_desc& d) {
 
 hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, int parts,
                         hipStream_t st, const void* x_gather, const float* w_fused,
-                        void* y_fused) {
+                        void* y_fused, bool* y_done) {
+  if (y_done) *y_done = false;
   const tr_moe_desc& d = p.d;
   if (d.T == 0) return hipSuccess;
   const int cus = device_cu_count();
@@ -1572,6 +1710,19 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   if (down && mode != kModeTiled) {
+    if (decode && y_done && g2.y) {
+      // the reduce folded in: y complete after this launch
+      const unsigned gy = static_cast<unsigned>(cdiv(d.H, 16) < cus ? cdiv(d.H, 16) : cus);
+      if (dec8_down)
+        hipLaunchKernelGGL((gemm_decode_y<8>), dim3(gy), dim3(kDecThreads), 0, st, g2,
+                           p.row_map, p.R_cap);
+      else
+        hipLaunchKernelGGL((gemm_decode_y<16>), dim3(gy), dim3(kDecThreads), 0, st, g2,
+                           p.row_map, p.R_cap);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+      *y_done = true;
+      return hipSuccess;
+    }
     if (decode && dec8_down)
       hipLaunchKernelGGL((gemm_decode<false, 8>), dim3(gd2), dim3(kDecThreads), 0, st, g2, I);
     else if (decode)

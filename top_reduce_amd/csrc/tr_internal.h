@@ -30,10 +30,13 @@ enum { kGemmUp = 1, kGemmDown = 2 };
 // route table instead of Xe, so no expand pass is needed.
 // With y_fused (bf16 only), GEMM2 writes the rows of received rows with one
 // local slot straight to y, weighted (w_fused, NULL for 1) and rounded as the
-// reduce would; combine_reduce with skip_single then completes y.
+// reduce would; combine_reduce with skip_single then completes y. With
+// y_done as well, a decode batch may run the whole reduce inside GEMM2: then
+// *y_done is set and y is complete (no combine_reduce needed).
 hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, int parts,
                         hipStream_t st, const void* x_gather = nullptr,
-                        const float* w_fused = nullptr, void* y_fused = nullptr);
+                        const float* w_fused = nullptr, void* y_fused = nullptr,
+                        bool* y_done = nullptr);
 // Whether GEMM1 may gather from x of this shape (32-bit buffer offsets).
 bool gemm_can_gather(const tr_moe_desc& d);
 hipError_t combine_reduce(const tr_moe_plan& p, const void* expert_out, const float* w, void* y,
