@@ -207,7 +207,10 @@ tr_status moe_compact_rows(int64_t T, int32_t block_rows, const int32_t* block_c
  * reduce): Xe is not written, and O only for received rows with several
  * local slots. With enough tiles for several rounds the two GEMMs run as
  * three launches (GEMM1's whole rounds; its last round beside GEMM2 tiles of
- * rows GEMM1 has finished; the rest of GEMM2), with the same result. */
+ * rows GEMM1 has finished; the rest of GEMM2), with the same result. A
+ * decode batch (at most 32 expanded rows, automatic GEMM mode) runs the
+ * reduce inside GEMM2's launch, again with the same result, and writes no O
+ * (DeepEP issue #760, body: the separate low-batch epilogue left out). */
 tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_weights,
                       const void* w1, const void* w2, void* y, hipStream_t stream);
 
