@@ -74,8 +74,9 @@ typedef enum { TR_BF16 = 0, TR_F32 = 1 } tr_dtype;
 typedef enum { TR_IDX_I32 = 0, TR_IDX_I64 = 1 } tr_idx_dtype;
 
 /* Grouped-GEMM kernel choice. AUTO sends experts with at most 32 routes to the
- * weight-streaming kernel and the others to the tiled MFMA kernel; the FORCE
- * flags send every expert to one of them (for testing). */
+ * weight-streaming kernel and the others to the tiled MFMA kernel, and every
+ * expert to the weight-streaming kernel when T * K <= 128; the FORCE flags
+ * send every expert to one of them (for testing). */
 #define TR_FLAG_GEMM_FORCE_TILED 0x1
 #define TR_FLAG_GEMM_FORCE_STREAM 0x2
 /* No expanded-row buffer: the workspace holds no Xe (it shrinks by
@@ -117,10 +118,10 @@ typedef struct tr_moe_plan {
                               experts, entries of tok_rest, rows that carry a
                               token (T, or the carrying rows of a padded plan),
                               non-empty experts the streaming GEMM takes (fewer
-                              than 33 routes; every one with
-                              TR_FLAG_GEMM_FORCE_STREAM, none with
-                              TR_FLAG_GEMM_FORCE_TILED), non-empty experts the
-                              tiled GEMM takes (the others) */
+                              than 33 routes, any number when T * K <= 128;
+                              every one with TR_FLAG_GEMM_FORCE_STREAM, none
+                              with TR_FLAG_GEMM_FORCE_TILED), non-empty experts
+                              the tiled GEMM takes (the others) */
     int32_t* scan_tmp;     /* route-scan block partials */
     void* Xe;              /* [R_cap + 256, H] expanded rows (expert-contiguous);
                               NULL with TR_FLAG_NO_XE */
@@ -239,8 +240,9 @@ tr_status moe_grouped_gemm_up_x(const tr_moe_plan* plan, const void* x, const vo
 tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStream_t stream);
 /* GEMM2 with the weighted reduce folded into its epilogue for received rows
  * with exactly one local slot whose expert the tiled kernel takes (more than
- * 32 routes; every expert with TR_FLAG_GEMM_FORCE_TILED, none with
- * TR_FLAG_GEMM_FORCE_STREAM): the plan's row_dst. Such a row's output is
+ * 32 routes in a batch of T * K > 128; every expert with
+ * TR_FLAG_GEMM_FORCE_TILED, none with TR_FLAG_GEMM_FORCE_STREAM): the plan's
+ * row_dst. Such a row's output is
  * rounded to bf16 as O would be, weighted and rounded again exactly as
  * moe_combine_reduce does, and written straight to y[t]; the other rows go to
  * O. topk_weights: device fp32 [T, K] or NULL (weight 1); y: device [T, H],

@@ -50,8 +50,11 @@ def _check_route(idx_np, E, B, counts, idx_dtype=torch.int64, flags=0):
     assert int(v["stats"][5]) == int(carry.sum())
     # experts of the streaming and of the tiled GEMM, per the plan's mode
     c = ref["counts"]
+    # (the automatic mode streams every expert of a batch of at most 128
+    # expanded rows)
     lo = (1 if flags & tr.FLAG_GEMM_FORCE_TILED
-          else np.iinfo(np.int64).max if flags & tr.FLAG_GEMM_FORCE_STREAM else 33)
+          else np.iinfo(np.int64).max if flags & tr.FLAG_GEMM_FORCE_STREAM or T * K <= 128
+          else 33)
     assert int(v["stats"][6]) == int(((c > 0) & (c < lo)).sum())
     assert int(v["stats"][7]) == int((c >= lo).sum())
     # padding rows are among the rows the reduce writes (as +0)

@@ -21,8 +21,11 @@ def _check(idx_np, E, eb=0, idx_dtype=torch.int64, H=256, I=128, flags=0):
     idx = torch.from_numpy(np.ascontiguousarray(idx_np)).to(idx_dtype).cuda()
     p = tr.plan(idx, E=E, H=H, I=I, dtype=torch.bfloat16, expert_begin=eb, flags=flags)
     # fewest routes of an expert the tiled GEMM takes, per the plan's mode
+    # (the automatic mode streams every expert of a batch of at most 128
+    # expanded rows)
     lo = (1 if flags & tr.FLAG_GEMM_FORCE_TILED
-          else np.iinfo(np.int64).max if flags & tr.FLAG_GEMM_FORCE_STREAM else 33)
+          else np.iinfo(np.int64).max if flags & tr.FLAG_GEMM_FORCE_STREAM or T * K <= 128
+          else 33)
     stats = tr.plan_stats(p)
     v = p.views()
     ref = oracle.route(idx_np, E, eb)

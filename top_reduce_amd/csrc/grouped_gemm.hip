@@ -1570,8 +1570,13 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   const tr_moe_desc& d = p.d;
   if (d.T == 0) return hipSuccess;
   const int cus = device_cu_count();
-  const int mode = (d.flags & TR_FLAG_GEMM_FORCE_STREAM) ? kModeStream
-                   : (d.flags & TR_FLAG_GEMM_FORCE_TILED) ? kModeTiled : kModeAuto;
+  // A small batch in the automatic mode streams every expert (the route scan
+  // assumed as much when it marked rows for the reduce folded into GEMM2;
+  // at most kStreamMaxRows expanded rows no expert can have more anyway).
+  int mode = kModeAuto;
+  if (d.flags & TR_FLAG_GEMM_FORCE_TILED) mode = kModeTiled;
+  else if (d.flags & TR_FLAG_GEMM_FORCE_STREAM) mode = kModeStream;
+  else if (p.R_cap > kStreamMaxRows && p.R_cap <= kSmallBatchRows) mode = kModeStream;
   const int E = d.E;
   const int I = static_cast<int>(d.I);
   const bool up = parts & kGemmUp, down = parts & kGemmDown;
@@ -1689,7 +1694,7 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   // A decode batch (AUTO mode, at most kStreamMaxRows expanded rows, so no
   // tiled experts): the latency-minded kernel, one block per unit up to one
   // per CU.
-  const bool decode = !tiled && mode == kModeAuto;
+  const bool decode = mode == kModeAuto && p.R_cap <= kStreamMaxRows;
   const unsigned gd1 = static_cast<unsigned>(u1 < cus ? u1 : cus);
   const unsigned gd2 = static_cast<unsigned>(u2 < cus ? u2 : cus);
   // each wave's share of k32 blocks: chunks of 8 when it fits, else 16

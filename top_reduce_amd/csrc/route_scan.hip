@@ -682,8 +682,7 @@ hipError_t launch(const tr_moe_plan& p, const IdxT* idx, hipStream_t st) {
   const int B = p.block_rows;
   const int* bc = p.block_counts;
   // fewest routes of an expert the grouped GEMM tiles (the others stream)
-  const int min_tiled = (d.flags & TR_FLAG_GEMM_FORCE_STREAM) ? INT32_MAX
-                        : (d.flags & TR_FLAG_GEMM_FORCE_TILED) ? 1 : kStreamMaxRows + 1;
+  const int min_tiled = min_tiled_routes(d);
   if (d.T * K <= kSmallSlots) {
     const int T = static_cast<int>(d.T), TK = T * K;
     if (TK <= 64)

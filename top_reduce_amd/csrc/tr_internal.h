@@ -12,6 +12,17 @@ constexpr int kMaxK = 32;
 constexpr int kMaxE = 1024;
 // Experts with at most this many routes go to the weight-streaming GEMM.
 constexpr int kStreamMaxRows = 32;
+// A batch of at most this many expanded rows (T * K) sends every expert to the
+// weight-streaming GEMM in the automatic mode: such experts rarely fill a
+// tile, and the tiled kernels' launches would mostly find nothing to do.
+constexpr int kSmallBatchRows = 128;
+// The fewest routes of an expert the tiled GEMM takes under d's flags (the
+// route scan marks the rows of such experts for the reduce folded into GEMM2).
+inline int min_tiled_routes(const tr_moe_desc& d) {
+  if (d.flags & TR_FLAG_GEMM_FORCE_STREAM) return 0x7fffffff;
+  if (d.flags & TR_FLAG_GEMM_FORCE_TILED) return 1;
+  return d.T * d.K <= kSmallBatchRows ? 0x7fffffff : kStreamMaxRows + 1;
+}
 // Spare rows after R_cap in the expanded (Xe) and intermediate (h) buffers,
 // so GEMM tiles may read a full tile of rows from any segment start.
 constexpr int kRowPad = 256;
