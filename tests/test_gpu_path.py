@@ -315,6 +315,45 @@ def test_decode_forward_equals_stages(name, T, variant):
     ref = oracle.forward(wl.x, wl.idx, wl.weights, wl.w1, wl.w2, wl.E)
     y = host(tr.forward(p, d["x"], d["w"], d["w1"], d["w2"]))
     _assert_close(as_f64(y), ref, wl.dtype, f"{name} decode y")
+    # y aliasing x (GEMM1 has read x before GEMM2 writes y)
+    xa = d["x"].clone()
+    y_al = tr.forward(p, xa, d["w"], d["w1"], d["w2"], y=xa)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y_al), y)
+
+
+def test_decode_forward_duplicates_and_padding():
+    """Decode batches with the same local expert twice in one row, and a
+    DP-padded plan whose padding rows hold stale local ids: the forward
+    (reduce inside GEMM2) equals the stages bit for bit and the oracle on the
+    carrying rows; padding rows are +0."""
+    wl = gen.make_workload("decode_k8", with_weights=True)
+    idx = wl.idx.copy()
+    idx[0, :3] = 2                      # expert 2 three times in row 0
+    idx[1, :] = -1                      # a row with no route
+    idx[2, 1] = idx[2, 0] = 5
+    d = upload(wl)
+    di = dev(idx)
+    p = tr.plan(di, E=wl.E, H=wl.H, I=wl.I)
+    y_f = tr.forward(p, d["x"], d["w"], d["w1"], d["w2"])
+    tr.expand(p, d["x"])
+    tr.grouped_gemm(p, d["w1"], d["w2"])
+    y_s = tr.combine_reduce(p, d["w"])
+    torch.cuda.synchronize()
+    assert torch.equal(y_f.view(torch.int16), y_s.view(torch.int16))
+    ref = oracle.forward(wl.x, idx, wl.weights, wl.w1, wl.w2, wl.E)
+    _assert_close(as_f64(host(y_f)), ref, wl.dtype, "decode duplicates y")
+    # padded: blocks of 2 rows, the second block carries one row
+    bc = torch.tensor([2, 1], dtype=torch.int32, device="cuda")
+    stale = idx.copy()
+    stale[3] = np.arange(wl.K) % wl.E   # padding row with local ids
+    pp = tr.plan(dev(stale), E=wl.E, H=wl.H, I=wl.I, block_rows=2, block_counts=bc)
+    y_p = host(tr.forward(pp, d["x"], d["w"], d["w1"], d["w2"]))
+    carry = np.array([True, True, True, False])
+    ref_p = oracle.forward(wl.x, np.where(carry[:, None], stale, -1), wl.weights, wl.w1, wl.w2,
+                           wl.E)
+    _assert_close(as_f64(y_p), ref_p, wl.dtype, "decode padded y")
+    assert (y_p[~carry] == 0).all()
 
 
 @pytest.mark.parametrize("name,flags,T", [("mid", 0, None), ("mid", tr.FLAG_GEMM_FORCE_TILED, None),
