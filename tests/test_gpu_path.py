@@ -322,6 +322,24 @@ def test_decode_forward_equals_stages(name, T, variant):
     assert np.array_equal(host(y_al), y)
 
 
+# fewer expanded rows than one 256-row m-tile, experts of many rows (the
+# tiled kernel when forced, or in the automatic mode past 128 rows)
+gen.custom_spec("few_rows_big_experts", T=64, K=2, E=2, G=2, H=512, I=256, zipf_s=0.0, seed=17)
+gen.custom_spec("few_rows_192", T=96, K=2, E=2, G=2, H=512, I=256, zipf_s=0.0, seed=18)
+
+
+@pytest.mark.parametrize("name,flags", [("few_rows_big_experts", 0),
+                                        ("few_rows_big_experts", tr.FLAG_GEMM_FORCE_TILED),
+                                        ("few_rows_192", 0),
+                                        ("few_rows_192", tr.FLAG_GEMM_FORCE_TILED)])
+def test_forward_fewer_rows_than_a_tile(name, flags):
+    say(f"forward {name} flags={flags}")
+    wl = gen.make_workload(name, with_weights=True)
+    _, y = _forward(wl, flags)
+    ref = oracle.forward(wl.x, wl.idx, wl.weights, wl.w1, wl.w2, wl.E)
+    _assert_close(as_f64(y), ref, wl.dtype, f"{name} y")
+
+
 def test_decode_forward_duplicates_and_padding():
     """Decode batches with the same local expert twice in one row, and a
     DP-padded plan whose padding rows hold stale local ids: the forward
