@@ -129,3 +129,22 @@ def test_route_deterministic():
         assert torch.equal(a[f], b[f]), f
     for f in ("row_src", "row_k"):          # defined for the first R rows only
         assert torch.equal(a[f][:R], b[f][:R]), f
+
+
+@pytest.mark.parametrize("i", range(60))
+def test_route_random_shapes(i):
+    """Seeded random shapes on both sides of every kernel switch (one block
+    of 64 / 256 / 1024 threads, the general single block, two kernels with
+    few or many blocks; 1 to 1024 experts; K up to 32; int32 ids; foreign and
+    shifted ids; every GEMM mode), bit-exact against the oracle."""
+    rng = np.random.default_rng(2000 + i)
+    K = int(rng.choice([1, 2, 3, 4, 8, 16, 32]))
+    T = int(rng.choice([1, 3, 16, 63, 100, 300, 1000, 3000, 20000, 60000]))
+    T = max(1, min(T, 200000 // K))
+    E = int(rng.choice([1, 2, 7, 28, 64, 100, 256, 1000, 1024]))
+    lo, hi = -3, E + int(rng.integers(0, 3 * E + 1))
+    idx = rng.integers(lo, hi, size=(T, K))
+    eb = int(rng.choice([0, 0, 5, E]))
+    flags = int(rng.choice([0, 0, tr.FLAG_GEMM_FORCE_TILED, tr.FLAG_GEMM_FORCE_STREAM]))
+    dt = torch.int32 if rng.random() < 0.3 else torch.int64
+    _check(np.where(idx >= 0, idx + eb, idx), E, eb=eb, idx_dtype=dt, flags=flags)
