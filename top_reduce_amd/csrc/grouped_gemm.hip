@@ -925,7 +925,10 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
     cntv[j] = j * kThreads < a.E ? a.counts[e] : 0;
   }
   asm volatile("" : : : "memory");   // the loads above go out before the exit test
-  if (take == 0) return;
+  // take experts give take * (units per expert) units, one per block in
+  // turn: a block past them has none (the grid is sized for all E experts)
+  if (static_cast<int>(blockIdx.x) >= take * ((a.Nc + (kSwiglu ? 8 : 16) - 1) / (kSwiglu ? 8 : 16)))
+    return;
   const int mode = a.mode;
   const int n_elig = expert_prefix(a.counts, a.E, [mode](int c) {
     return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
