@@ -289,11 +289,13 @@ def test_forward_fused_equals_stages(name, flags, T):
 # decode batches (at most 32 expanded rows): the forward runs the reduce
 # inside GEMM2; one local expert, several, every slot local (dense), K = 8
 gen.custom_spec("decode_k8", T=4, K=8, E=12, G=24, H=512, I=256, zipf_s=0.3, seed=16)
+# more than 64 local experts (the decode kernels' block-wide expert table)
+gen.custom_spec("decode_e100", T=2, K=16, E=100, G=100, H=512, I=256, zipf_s=0.0, seed=19)
 
 
 @pytest.mark.parametrize("name,T,variant", [("c3", 1, ""), ("c3", 2, ""), ("c3", 1, "random"),
                                             ("c3", 2, "random"), ("c3", 2, "dense"),
-                                            ("decode_k8", None, "")])
+                                            ("decode_k8", None, ""), ("decode_e100", None, "")])
 def test_decode_forward_equals_stages(name, T, variant):
     """A decode forward (GEMM2 with the reduce folded in) equals the unfused
     composition expand -> grouped GEMM -> reduce bit for bit, with and without

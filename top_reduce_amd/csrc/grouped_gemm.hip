@@ -1061,6 +1061,74 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
 
+// The experts the decode kernels take (every non-empty one the mode streams),
+// in expert order. With at most 64 experts every wave finds them on its own:
+// lane e holds expert e's count and offset, a ballot marks the eligible
+// ones, and the q-th is the set bit with q set bits below it (no LDS, no
+// barrier before the first weight load). With more, the block-wide prefix
+// and LDS tables.
+struct DecodeExperts {
+  int n;                  // eligible experts
+  bool wave;              // the wave form (E <= 64)
+  uint64_t mask;          // wave form: the eligible experts' lanes
+  int cnt_l, off_l;       // wave form: this lane's expert's count and offset
+  __device__ __forceinline__ void get(int q, const int* list, const int* cnt_s,
+                                      const int* off_s, int& e, int& cnt, int& off) const {
+    if (wave) {
+      const uint64_t hit =
+          __ballot(((mask >> __lane_id()) & 1) && popc_below(mask) == q);
+      e = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      cnt = __shfl(cnt_l, e, kWave);
+      off = __shfl(off_l, e, kWave);
+    } else {
+      e = list[q];
+      cnt = cnt_s[e];
+      off = off_s[e];
+    }
+  }
+};
+
+template <int kBlock>
+__device__ __forceinline__ DecodeExperts decode_experts(const GemmArgs& a, int* pre, int* tmp,
+                                                        int* list, int* cnt_s, int* off_s) {
+  DecodeExperts ex{};
+  const int mode = a.mode;
+  if (a.E <= kWave) {
+    const int lane = __lane_id();
+    const int e = min(lane, a.E - 1);
+    const int c = a.counts[e], o = a.offsets[e];
+    ex.wave = true;
+    ex.mask = __ballot(lane < a.E && c > 0 && goes_to_stream(c, mode));
+    ex.n = __popcll(ex.mask);
+    ex.cnt_l = c;
+    ex.off_l = o;
+    return ex;
+  }
+  // the counts and offsets, loaded together with the prefix's
+  int offv[kMaxE / kBlock], cntv[kMaxE / kBlock];
+#pragma unroll
+  for (int j = 0; j < kMaxE / kBlock; ++j) {
+    const int e = min(static_cast<int>(threadIdx.x) + j * kBlock, a.E - 1);
+    offv[j] = j * kBlock < a.E ? a.offsets[e] : 0;
+    cntv[j] = j * kBlock < a.E ? a.counts[e] : 0;
+  }
+  ex.wave = false;
+  ex.n = expert_prefix<kBlock>(a.counts, a.E, [mode](int c) {
+    return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
+  }, pre, tmp);
+#pragma unroll
+  for (int j = 0; j < kMaxE / kBlock; ++j) {
+    const int e = threadIdx.x + j * kBlock;
+    if (e < a.E) {
+      if (pre[e + 1] > pre[e]) list[pre[e]] = e;
+      cnt_s[e] = cntv[j];
+      off_s[e] = offv[j];
+    }
+  }
+  __syncthreads();
+  return ex;
+}
+
 // kDecB: k32 blocks per chunk (8 or 16, the launch picks the one that fits a
 // wave's share with the fewest spare loads).
 template <bool kSwiglu, int kDecB>
@@ -1071,29 +1139,9 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode(GemmArgs a, int I) {
   __shared__ int tmp[kDecWaves];
   __shared__ floatx4 red[kDecWaves][kWave];
 
-  // the experts' counts and offsets, loaded together with the prefix's
-  int offv[kMaxE / kDecThreads], cntv[kMaxE / kDecThreads];
-#pragma unroll
-  for (int j = 0; j < kMaxE / kDecThreads; ++j) {
-    const int e = min(static_cast<int>(threadIdx.x) + j * kDecThreads, a.E - 1);
-    offv[j] = j * kDecThreads < a.E ? a.offsets[e] : 0;
-    cntv[j] = j * kDecThreads < a.E ? a.counts[e] : 0;
-  }
-  const int mode = a.mode;
-  const int n_elig = expert_prefix<kDecThreads>(a.counts, a.E, [mode](int c) {
-    return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
-  }, pre, tmp);
+  const DecodeExperts ex = decode_experts<kDecThreads>(a, pre, tmp, list, cnt_s, off_s);
+  const int n_elig = ex.n;
   if (n_elig == 0) return;
-#pragma unroll
-  for (int j = 0; j < kMaxE / kDecThreads; ++j) {
-    const int e = threadIdx.x + j * kDecThreads;
-    if (e < a.E) {
-      if (pre[e + 1] > pre[e]) list[pre[e]] = e;
-      cnt_s[e] = cntv[j];
-      off_s[e] = offv[j];
-    }
-  }
-  __syncthreads();
 
   const int cols = kSwiglu ? 8 : 16;               // outputs per unit
   const int upe = (a.Nc + cols - 1) / cols;        // units per expert
@@ -1111,10 +1159,9 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode(GemmArgs a, int I) {
   uint16_t* __restrict__ Cb = static_cast<uint16_t*>(a.C);
 
   for (int u = blockIdx.x; u < total; u += gridDim.x) {
-    const int e = list[u / upe];
+    int e, cnt, off;
+    ex.get(u / upe, list, cnt_s, off_s, e, cnt, off);
     const int c = u % upe;
-    const int cnt = cnt_s[e];
-    const int off = off_s[e];
     int64_t wrow;
     if (kSwiglu) {
       const int col = min(c * 8 + (arow & 7), I - 1);
@@ -1217,35 +1264,17 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_y(GemmArgs a,
 
   const int tid = threadIdx.x;
   const int TK = static_cast<int>(a.T) * a.K;   // <= kStreamMaxRows
-  int offv[kMaxE / kDecThreads], cntv[kMaxE / kDecThreads];
-#pragma unroll
-  for (int j = 0; j < kMaxE / kDecThreads; ++j) {
-    const int e = min(tid + j * kDecThreads, a.E - 1);
-    offv[j] = j * kDecThreads < a.E ? a.offsets[e] : 0;
-    cntv[j] = j * kDecThreads < a.E ? a.counts[e] : 0;
-  }
   int mv = -1;
   if (tid < TK) {
     mv = row_map[tid];
     if (mv >= n_rows) mv = -1;
   }
-  const int mode = a.mode;
-  const int n_elig = expert_prefix<kDecThreads>(a.counts, a.E, [mode](int c) {
-    return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
-  }, pre, tmp);
-#pragma unroll
-  for (int j = 0; j < kMaxE / kDecThreads; ++j) {
-    const int e = tid + j * kDecThreads;
-    if (e < a.E) {
-      if (pre[e + 1] > pre[e]) list[pre[e]] = e;
-      cnt_s[e] = cntv[j];
-      off_s[e] = offv[j];
-    }
-  }
+  const DecodeExperts ex = decode_experts<kDecThreads>(a, pre, tmp, list, cnt_s, off_s);
+  const int n_elig = ex.n;
+  // (map_s is read only after the barrier that stores w_s)
   if (tid < TK) map_s[tid] = mv;
   // the local slots' weights: needed only after the first unit's MFMAs
   const float wv = (tid < TK && mv >= 0 && a.wts) ? a.wts[tid] : 1.0f;
-  __syncthreads();
 
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -1264,9 +1293,8 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_y(GemmArgs a,
   for (int c = blockIdx.x; c < n_units; c += gridDim.x) {
     const int64_t wrow = min(c * 16 + arow, a.Nc - 1);
     for (int q = 0; q < n_elig; ++q) {
-      const int e = list[q];
-      const int cnt = cnt_s[e];
-      const int off = off_s[e];
+      int e, cnt, off;
+      ex.get(q, list, cnt_s, off_s, e, cnt, off);
       const uint16_t* wp = Bb + (static_cast<int64_t>(e) * Nb + wrow) * Kd + g * 8;
       for (int tb = 0; tb < cnt; tb += 16) {
         const int tok = tb + arow;
