@@ -862,6 +862,75 @@ __global__ __launch_bounds__(kThreads) void gemm_hybrid(GemmArgs g1, GemmArgs g2
 // --------------------------------------------------------------------------
 // Weight-streaming kernel (bf16, experts with few rows)
 // --------------------------------------------------------------------------
+// The experts the streaming and decode kernels take (every non-empty one the
+// mode streams),
+// in expert order. With at most 64 experts every wave finds them on its own:
+// lane e holds expert e's count and offset, a ballot marks the eligible
+// ones, and the q-th is the set bit with q set bits below it (no LDS, no
+// barrier before the first weight load). With more, the block-wide prefix
+// and LDS tables.
+struct StreamExperts {
+  int n;                  // eligible experts
+  bool wave;              // the wave form (E <= 64)
+  uint64_t mask;          // wave form: the eligible experts' lanes
+  int cnt_l, off_l;       // wave form: this lane's expert's count and offset
+  __device__ __forceinline__ void get(int q, const int* list, const int* cnt_s,
+                                      const int* off_s, int& e, int& cnt, int& off) const {
+    if (wave) {
+      const uint64_t hit =
+          __ballot(((mask >> __lane_id()) & 1) && popc_below(mask) == q);
+      e = __ffsll(static_cast<unsigned long long>(hit)) - 1;
+      cnt = __shfl(cnt_l, e, kWave);
+      off = __shfl(off_l, e, kWave);
+    } else {
+      e = list[q];
+      cnt = cnt_s[e];
+      off = off_s[e];
+    }
+  }
+};
+
+template <int kBlock>
+__device__ __forceinline__ StreamExperts stream_experts(const GemmArgs& a, int* pre, int* tmp,
+                                                        int* list, int* cnt_s, int* off_s) {
+  StreamExperts ex{};
+  const int mode = a.mode;
+  if (a.E <= kWave) {
+    const int lane = __lane_id();
+    const int e = min(lane, a.E - 1);
+    const int c = a.counts[e], o = a.offsets[e];
+    ex.wave = true;
+    ex.mask = __ballot(lane < a.E && c > 0 && goes_to_stream(c, mode));
+    ex.n = __popcll(ex.mask);
+    ex.cnt_l = c;
+    ex.off_l = o;
+    return ex;
+  }
+  // the counts and offsets, loaded together with the prefix's
+  int offv[kMaxE / kBlock], cntv[kMaxE / kBlock];
+#pragma unroll
+  for (int j = 0; j < kMaxE / kBlock; ++j) {
+    const int e = min(static_cast<int>(threadIdx.x) + j * kBlock, a.E - 1);
+    offv[j] = j * kBlock < a.E ? a.offsets[e] : 0;
+    cntv[j] = j * kBlock < a.E ? a.counts[e] : 0;
+  }
+  ex.wave = false;
+  ex.n = expert_prefix<kBlock>(a.counts, a.E, [mode](int c) {
+    return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
+  }, pre, tmp);
+#pragma unroll
+  for (int j = 0; j < kMaxE / kBlock; ++j) {
+    const int e = threadIdx.x + j * kBlock;
+    if (e < a.E) {
+      if (pre[e + 1] > pre[e]) list[pre[e]] = e;
+      cnt_s[e] = cntv[j];
+      off_s[e] = offv[j];
+    }
+  }
+  __syncthreads();
+  return ex;
+}
+
 constexpr int kStreamU = 8;  // k32 blocks per unrolled step
 
 // This wave's k32 blocks [kb0, kb1) of one token group: NQ groups of 16 rows
@@ -917,33 +986,13 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
   // clamped so that the loads are unconditional); a launch for which the
   // route scan counted no expert (a.n_take) exits before the prefix
   const int take = *a.n_take;
-  int offv[kMaxE / kThreads], cntv[kMaxE / kThreads];
-#pragma unroll
-  for (int j = 0; j < kMaxE / kThreads; ++j) {
-    const int e = min(static_cast<int>(threadIdx.x) + j * kThreads, a.E - 1);
-    offv[j] = j * kThreads < a.E ? a.offsets[e] : 0;
-    cntv[j] = j * kThreads < a.E ? a.counts[e] : 0;
-  }
-  asm volatile("" : : : "memory");   // the loads above go out before the exit test
   // take experts give take * (units per expert) units, one per block in
   // turn: a block past them has none (the grid is sized for all E experts)
   if (static_cast<int>(blockIdx.x) >= take * ((a.Nc + (kSwiglu ? 8 : 16) - 1) / (kSwiglu ? 8 : 16)))
     return;
-  const int mode = a.mode;
-  const int n_elig = expert_prefix(a.counts, a.E, [mode](int c) {
-    return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
-  }, pre, tmp);
+  const StreamExperts ex = stream_experts<kThreads>(a, pre, tmp, list, cnt_s, off_s);
+  const int n_elig = ex.n;
   if (n_elig == 0) return;
-#pragma unroll
-  for (int j = 0; j < kMaxE / kThreads; ++j) {
-    const int e = threadIdx.x + j * kThreads;
-    if (e < a.E) {
-      if (pre[e + 1] > pre[e]) list[pre[e]] = e;
-      cnt_s[e] = cntv[j];
-      off_s[e] = offv[j];
-    }
-  }
-  __syncthreads();
 
   const int cols = kSwiglu ? 8 : 16;               // outputs per unit
   const int upe = (a.Nc + cols - 1) / cols;        // units per expert
@@ -967,20 +1016,20 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
   auto ids_of = [&](int u, int (&id)[2]) {
     id[0] = id[1] = 0;
     if (u >= total || !a.gather) return;
-    const int e = list[u / upe];
+    int e, cnt, off;
+    ex.get(u / upe, list, cnt_s, off_s, e, cnt, off);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int t = q * 16 + arow;
-      if (t < cnt_s[e]) id[q] = a.gather[off_s[e] + t];
+      if (t < cnt) id[q] = a.gather[off + t];
     }
   };
   int id_next[2];
   ids_of(blockIdx.x, id_next);
   for (int u = blockIdx.x; u < total; u += gridDim.x) {
-    const int e = list[u / upe];
+    int e, cnt, off;
+    ex.get(u / upe, list, cnt_s, off_s, e, cnt, off);
     const int c = u % upe;
-    const int cnt = cnt_s[e];
-    const int off = off_s[e];
     const int id0[2] = {id_next[0], id_next[1]};
     ids_of(u + static_cast<int>(gridDim.x), id_next);
     int64_t wrow;
@@ -1061,73 +1110,6 @@ __global__ __launch_bounds__(kThreads) void gemm_stream(GemmArgs a, int I) {
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * kWave;
 
-// The experts the decode kernels take (every non-empty one the mode streams),
-// in expert order. With at most 64 experts every wave finds them on its own:
-// lane e holds expert e's count and offset, a ballot marks the eligible
-// ones, and the q-th is the set bit with q set bits below it (no LDS, no
-// barrier before the first weight load). With more, the block-wide prefix
-// and LDS tables.
-struct DecodeExperts {
-  int n;                  // eligible experts
-  bool wave;              // the wave form (E <= 64)
-  uint64_t mask;          // wave form: the eligible experts' lanes
-  int cnt_l, off_l;       // wave form: this lane's expert's count and offset
-  __device__ __forceinline__ void get(int q, const int* list, const int* cnt_s,
-                                      const int* off_s, int& e, int& cnt, int& off) const {
-    if (wave) {
-      const uint64_t hit =
-          __ballot(((mask >> __lane_id()) & 1) && popc_below(mask) == q);
-      e = __ffsll(static_cast<unsigned long long>(hit)) - 1;
-      cnt = __shfl(cnt_l, e, kWave);
-      off = __shfl(off_l, e, kWave);
-    } else {
-      e = list[q];
-      cnt = cnt_s[e];
-      off = off_s[e];
-    }
-  }
-};
-
-template <int kBlock>
-__device__ __forceinline__ DecodeExperts decode_experts(const GemmArgs& a, int* pre, int* tmp,
-                                                        int* list, int* cnt_s, int* off_s) {
-  DecodeExperts ex{};
-  const int mode = a.mode;
-  if (a.E <= kWave) {
-    const int lane = __lane_id();
-    const int e = min(lane, a.E - 1);
-    const int c = a.counts[e], o = a.offsets[e];
-    ex.wave = true;
-    ex.mask = __ballot(lane < a.E && c > 0 && goes_to_stream(c, mode));
-    ex.n = __popcll(ex.mask);
-    ex.cnt_l = c;
-    ex.off_l = o;
-    return ex;
-  }
-  // the counts and offsets, loaded together with the prefix's
-  int offv[kMaxE / kBlock], cntv[kMaxE / kBlock];
-#pragma unroll
-  for (int j = 0; j < kMaxE / kBlock; ++j) {
-    const int e = min(static_cast<int>(threadIdx.x) + j * kBlock, a.E - 1);
-    offv[j] = j * kBlock < a.E ? a.offsets[e] : 0;
-    cntv[j] = j * kBlock < a.E ? a.counts[e] : 0;
-  }
-  ex.wave = false;
-  ex.n = expert_prefix<kBlock>(a.counts, a.E, [mode](int c) {
-    return (c > 0 && goes_to_stream(c, mode)) ? 1 : 0;
-  }, pre, tmp);
-#pragma unroll
-  for (int j = 0; j < kMaxE / kBlock; ++j) {
-    const int e = threadIdx.x + j * kBlock;
-    if (e < a.E) {
-      if (pre[e + 1] > pre[e]) list[pre[e]] = e;
-      cnt_s[e] = cntv[j];
-      off_s[e] = offv[j];
-    }
-  }
-  __syncthreads();
-  return ex;
-}
 
 // kDecB: k32 blocks per chunk (8 or 16, the launch picks the one that fits a
 // wave's share with the fewest spare loads).
@@ -1139,7 +1121,7 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode(GemmArgs a, int I) {
   __shared__ int tmp[kDecWaves];
   __shared__ floatx4 red[kDecWaves][kWave];
 
-  const DecodeExperts ex = decode_experts<kDecThreads>(a, pre, tmp, list, cnt_s, off_s);
+  const StreamExperts ex = stream_experts<kDecThreads>(a, pre, tmp, list, cnt_s, off_s);
   const int n_elig = ex.n;
   if (n_elig == 0) return;
 
@@ -1269,7 +1251,7 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_y(GemmArgs a,
     mv = row_map[tid];
     if (mv >= n_rows) mv = -1;
   }
-  const DecodeExperts ex = decode_experts<kDecThreads>(a, pre, tmp, list, cnt_s, off_s);
+  const StreamExperts ex = stream_experts<kDecThreads>(a, pre, tmp, list, cnt_s, off_s);
   const int n_elig = ex.n;
   // (map_s is read only after the barrier that stores w_s)
   if (tid < TK) map_s[tid] = mv;
