@@ -1664,10 +1664,11 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   // With at most kStreamMaxRows expanded rows no expert can reach the tiled
   // kernel in AUTO mode: skip its launch (decode batches).
   const bool tiled = mode == kModeTiled || (mode == kModeAuto && p.R_cap > kStreamMaxRows);
-  // Both GEMMs with enough tiles for several rounds: three launches, GEMM2
-  // tiles filling GEMM1's last round (see early_down_tiles). The whole-round
-  // and hybrid launches share one grid, which the last one is told.
-  const bool split = up && down && tiled && t1 >= 2 * static_cast<int64_t>(cus);
+  // Both GEMMs with enough tiles for more than two rounds (by the bound
+  // above): three launches, GEMM2 tiles filling GEMM1's last round (see
+  // early_down_tiles). The whole-round and hybrid launches share one grid,
+  // which the last one is told.
+  const bool split = up && down && tiled && t1 > 2 * static_cast<int64_t>(cus);
   if (split) {
     const unsigned gsplit = gt1;
     if (g1.gather)
