@@ -22,8 +22,8 @@
  *   moe_forward  = moe_expand + moe_grouped_gemm + moe_combine_reduce; bf16
  *                runs the fused forms moe_grouped_gemm_up_x (GEMM1 straight
  *                from x), moe_grouped_gemm_down_y (GEMM2 writing rows with one
- *                local slot straight to y) and moe_combine_reduce_multi, with
- *                the same result bit for bit
+ *                local slot straight to y) and moe_combine_reduce_multi, fp32
+ *                moe_grouped_gemm_up_x, with the same result bit for bit
  *
  * Conventions for every entry point:
  *  - Pointers named "device" are HIP device (or managed) memory; the others
@@ -233,8 +233,9 @@ tr_status moe_grouped_gemm_up(const tr_moe_plan* plan, const void* w1, hipStream
 /* GEMM1 with the SwiGLU epilogue straight from the received rows: the
  * activation tiles are gathered from x (device [T, H]) through the plan's route
  * table, so no expand pass and no Xe are needed (the fused form of the
- * expand step). h equals moe_expand followed by moe_grouped_gemm_up. bf16 with
- * T * H * 2 < 2^31; otherwise it runs moe_expand and moe_grouped_gemm_up. */
+ * expand step). h equals moe_expand followed by moe_grouped_gemm_up. fp32, and
+ * bf16 with T * H * 2 < 2^31; otherwise (bf16 with a larger x) it runs
+ * moe_expand and moe_grouped_gemm_up. */
 tr_status moe_grouped_gemm_up_x(const tr_moe_plan* plan, const void* x, const void* w1,
                                 hipStream_t stream);
 tr_status moe_grouped_gemm_down(const tr_moe_plan* plan, const void* w2, hipStream_t stream);

@@ -219,7 +219,7 @@ def test_up_x_equals_expand_then_up(name, flags):
     """GEMM1 gathering the received rows through the route table computes the
     same h, bit for bit, as expand followed by GEMM1 over Xe: the same rows
     reach the same tile positions and the arithmetic order is unchanged (fp32
-    takes the expand route inside the call)."""
+    gathers as well)."""
     say(f"up_x {name} flags={flags}")
     wl = gen.make_workload(name, with_weights=True)
     d = upload(wl)

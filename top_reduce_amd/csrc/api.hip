@@ -285,8 +285,8 @@ tr_status moe_grouped_gemm_up_x(const tr_moe_plan* plan, const void* x, const vo
   if ((s = check_buf(x, "x", any)) != TR_OK) return s;
   if ((s = check_buf(w1, "w1", any)) != TR_OK) return s;
   if (!any) return ok();
-  if (!tr::gemm_can_gather(plan->d)) {
-    // fp32, or x past 2 GiB: expand first, then GEMM1 over Xe
+  if (plan->d.dtype == TR_BF16 && !tr::gemm_can_gather(plan->d)) {
+    // bf16 with x past 2 GiB: expand first, then GEMM1 over Xe
     if ((s = hip_status(tr::expand(*plan, x, stream), "moe_expand launch")) != TR_OK) return s;
     return hip_status(tr::grouped_gemm(*plan, w1, nullptr, tr::kGemmUp, stream),
                       "moe_grouped_gemm_up launch");
@@ -369,6 +369,12 @@ tr_status moe_forward(const tr_moe_plan* plan, const void* x, const float* topk_
     if (y_done) return ok();   // a decode batch: GEMM2 ran the reduce
     return hip_status(tr::combine_reduce(*plan, nullptr, topk_weights, y, stream, true),
                       "moe_combine_reduce launch");
+  } else if (plan->d.dtype == TR_F32) {
+    // fp32: GEMM1 reads x through the route table too (no expand pass);
+    // GEMM2 writes O for every row and the reduce takes them all
+    if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream, x),
+                        "moe_grouped_gemm launch")) != TR_OK)
+      return s;
   } else {
     if ((s = hip_status(tr::expand(*plan, x, stream), "moe_expand launch")) != TR_OK) return s;
     if ((s = hip_status(tr::grouped_gemm(*plan, w1, w2, tr::kGemmUp | tr::kGemmDown, stream),

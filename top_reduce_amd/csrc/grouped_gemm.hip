@@ -1396,7 +1396,12 @@ __global__ __launch_bounds__(kThreads) void gemm_f32(GemmArgs a, int I) {
     const int col = nt * F_BN + lr;
     const bool cv = col < a.Nc;
     const float* we = Bf + static_cast<int64_t>(e) * Nb * Kd;
-    const float* ap = lr < rows_valid ? Af + static_cast<int64_t>(row0 + lr) * Kd : nullptr;
+    // GEMM1 from the received rows: row r of the segment order is row
+    // gather[r] of x
+    const int arow = row0 + lr;
+    const float* ap =
+        lr < rows_valid ? Af + static_cast<int64_t>(a.gather ? a.gather[arow] : arow) * Kd
+                        : nullptr;
     const float* gp = cv ? we + static_cast<int64_t>(col) * Kd : nullptr;
     const float* up = (kSwiglu && cv) ? we + static_cast<int64_t>(I + col) * Kd : nullptr;
     floatx4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
@@ -1596,7 +1601,7 @@ hipError_t grouped_gemm(const tr_moe_plan& p, const void* w1, const void* w2, in
   const int64_t a_rows = p.R_cap + kRowPad;
   GemmArgs g1{p.Xe, w1, p.h, p.counts, p.offsets, E, static_cast<int>(d.H), I, mode, a_rows,
               nullptr, nullptr, nullptr, nullptr, d.K, d.T};
-  if (x_gather && d.dtype == TR_BF16) {
+  if (x_gather) {
     // GEMM1 reads the received rows through the route table: no Xe
     g1.A = x_gather;
     g1.a_rows = d.T;
