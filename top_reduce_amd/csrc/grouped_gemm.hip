@@ -1350,7 +1350,7 @@ __global__ __launch_bounds__(kDecThreads) void gemm_decode_y(GemmArgs a,
 // weight rows past the last output column and k past the end load as zero (no
 // access); outputs are stored only for valid rows and columns. fp32 shapes are
 // small (the tiny fp32 workload), so tiles are small for parallelism and
-// operands come straight from global memory, four chunks of loads ahead of
+// operands come straight from global memory, eight chunks of loads ahead of
 // their MFMAs.
 constexpr int F_BM = 16, F_BN = 16, F_BK = 16;
 
@@ -1405,7 +1405,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f32(GemmArgs a, int I) {
     const float* gp = cv ? we + static_cast<int64_t>(col) * Kd : nullptr;
     const float* up = (kSwiglu && cv) ? we + static_cast<int64_t>(I + col) * Kd : nullptr;
     floatx4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-    constexpr int kChunks = 4;
+    constexpr int kChunks = 8;
     for (int k0 = 0; k0 < Kd; k0 += kChunks * F_BK) {
       float av[kChunks][4], gv[kChunks][4], uv[kChunks][4];
 #pragma unroll
