@@ -1,19 +1,23 @@
 #!/usr/bin/env python3
 """Throughput of one GPU's share of the expert-parallel MoE FFN on MI355X.
 
-One step = the whole hot path on one batch: moe_plan (route scan), then the
-kernels moe_forward runs (for bf16: grouped SwiGLU GEMM up gathering the
-received rows, GEMM down writing the rows of received rows with one local
-slot straight to the output, the weighted top-k reduce of the others; for
-fp32: expand, GEMM up, GEMM down, reduce) through their stage entry points, on synthetic inputs already resident
-in HBM. Default workload: the prefill shape
-(16384 received tokens, H=7168, I=2048, 32 local experts of 256, top-8, Zipf
-s=1.0 popularity), bf16.
+One step = the whole hot path on one batch: moe_plan (route scan), then
+moe_forward (grouped SwiGLU GEMM up gathering the received rows through the
+route table; for bf16, GEMM down writing the rows of received rows with one
+local slot straight to the output and the weighted top-k reduce of the others,
+or the whole reduce inside GEMM down for a decode batch; for fp32, GEMM down
+and the reduce), captured once in a HIP graph and replayed, on synthetic
+inputs already resident in HBM. The same kernels also run stage by stage
+through their entry points, with events between the stages, for the
+per-stage figures. Default workload: the prefill shape (16384 received
+tokens, H=7168, I=2048, 32 local experts of 256, top-8, Zipf s=1.0
+popularity), bf16.
 
 Prints ONE JSON line: tokens/s over the timed steps, the roofline of the
-dominant kernel (HIP events between the stages of every timed step, on the
-stream the kernels run on), per-stage rates, the low-batch combine latencies, a sampled parity check and the CPU oracle's rate on a bounded sample
-of the same workload.
+dominant kernels (the forward's GEMM launches, HIP events around moe_forward
+on the stream the kernels run on), per-stage rates, the low-batch combine
+latencies, a sampled parity check and the CPU oracle's rate on a bounded
+sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--config c5] [--gpus 1]
 """
@@ -99,6 +103,40 @@ def stored_traffic(kernel: str, config: str, src: str):
     if not (m_h and m_b) or m_h.group(1) != kernel_source_hash(src):
         return None
     return float(m_b.group(1))
+
+
+def forward_gemm_launches(bf16: bool, T: int, K: int, E: int, H: int, I: int, cus: int):
+    """The grouped-GEMM launches of moe_forward on a plan of this shape in the
+    automatic GEMM mode, by the library's host-side rules (tiles of 256 rows
+    and 256 columns, at most 32 expanded rows for the decode kernels, at most
+    128 for streaming every expert). Returns (GEMM1 gathers x through the
+    route table, GEMM2 writes single-slot rows to y and a reduce of the other
+    rows follows, GEMM2 does the whole reduce, kernel names in launch order)."""
+    cdiv = lambda a, b: -(-a // b)
+    if not bf16:
+        return True, False, False, ["gemm_f32<true> (GEMM1 gathering x)", "gemm_f32<false>"]
+    if T * H * 2 > 0x7FFFFFFF:   # 32-bit offsets: expand first, no fused writes to y
+        return False, False, False, ["gemm_tiled<true, false>", "gemm_stream<true>",
+                                     "gemm_tiled<false, false>", "gemm_stream<false>"]
+    if H % 256 or I % 128:
+        return True, True, False, ["gemm_any<true>", "gemm_any<false>"]
+    R_cap = T * K
+    if R_cap <= 32:
+        up = 8 if cdiv(cdiv(H, 32), 8) <= 8 else 16
+        down = 8 if cdiv(cdiv(I, 32), 8) <= 8 else 16
+        return True, True, True, [f"gemm_decode<true, {up}>",
+                                  f"gemm_decode_y<{down}> (GEMM2 with the reduce folded in)"]
+    if R_cap <= 128:
+        return True, True, False, ["gemm_stream<true>", "gemm_stream<false>"]
+    t1 = (cdiv(R_cap, 256) + E) * cdiv(I, 128)
+    if t1 > 2 * cus:
+        return True, True, False, ["gemm_tiled<true, true> (GEMM1 whole rounds)",
+                                   "gemm_stream<true> (experts with <= 32 rows)",
+                                   "gemm_hybrid<true> (GEMM1 last round beside early GEMM2 tiles)",
+                                   "gemm_tiled<false, false> (rest of GEMM2)",
+                                   "gemm_stream<false> (experts with <= 32 rows)"]
+    return True, True, False, ["gemm_tiled<true, true>", "gemm_stream<true> (experts with <= 32 rows)",
+                               "gemm_tiled<false, false>", "gemm_stream<false> (experts with <= 32 rows)"]
 
 
 def lowbatch_combine(reps: int):
@@ -492,12 +530,13 @@ def main():
         return
 
     # One step = plan (route scan) + forward: the same kernels moe_forward
-    # launches (bf16: GEMM up gathering x through the route table, GEMM down
-    # writing single-slot rows to y, the reduce of the other rows; fp32:
-    # expand, GEMM up over the expanded rows, GEMM down, reduce), called
-    # stage by stage so that events between the stages, on the launch stream,
-    # give each kernel's device time inside the timed region.
-    gather = bf16 and wl.T * wl.H * 2 <= 0x7FFFFFFF
+    # launches (GEMM up gathering x through the route table; bf16: GEMM down
+    # writing single-slot rows to y, the reduce of the other rows; fp32: GEMM
+    # down writing every expert row, the full reduce), called stage by stage
+    # so that events between the stages, on the launch stream, give each
+    # kernel's device time inside the timed region.
+    gather, fused, reduce_in_gemm2, launches = forward_gemm_launches(
+        bf16, wl.T, wl.K, wl.E, wl.H, wl.I, torch.cuda.get_device_properties(dev).multi_processor_count)
     stage_names = (("route_scan", "gemm_up", "gemm_down", "combine_reduce") if gather else
                    ("route_scan", "expand", "gemm_up", "gemm_down", "combine_reduce"))
 
@@ -516,13 +555,13 @@ def main():
             tr.grouped_gemm_up(q, w1, stream=stream)
         i += 1
         evs[i].record(stream)
-        if gather:
+        if fused:
             tr.grouped_gemm_down_y(q, w2, w, y, stream=stream)
         else:
             tr.grouped_gemm_down(q, w2, stream=stream)
         i += 1
         evs[i].record(stream)
-        if gather:
+        if fused:
             tr.combine_reduce_multi(q, w, y, stream=stream)
         else:
             tr.combine_reduce(q, w, y=y, stream=stream)
@@ -646,6 +685,7 @@ def main():
     }
     if gather:
         del work["expand"]
+    if fused:
         # the reduce reads the rows of received rows with several local slots
         # and writes those and the rows without a local slot
         work["combine_reduce"] = ("hbm", (R - n_single) * H * b + (T - n_single) * H * b + 8 * T * K)
@@ -679,16 +719,13 @@ def main():
                          "peak": peak_mm, "frac": ach / peak_mm, "algorithmic_flops": amount}
         stages[k].update(extra)
     # The dominant kernels: the forward's GEMM launches (both projections,
-    # 95% of a prefill step), timed inside the forward as the library runs it.
-    gemm_fwd_us = fwd_us - us["combine_reduce"] - (0.0 if gather else us["expand"])
+    # 95% of a prefill step), timed inside the forward as the library runs it:
+    # the forward's time minus its reduce launch, if it makes one.
+    gemm_fwd_us = (fwd_us - (0.0 if reduce_in_gemm2 else us["combine_reduce"])
+                   - (0.0 if gather else us["expand"]))
     both_flops = 6.0 * R * H * I
     both_bytes = gemm_bytes["gemm_up"] + gemm_bytes["gemm_down"]
     t_gemm = gemm_fwd_us / 1e6
-    launches = (["gemm_tiled<true, true> (GEMM1 whole rounds)",
-                 "gemm_hybrid<true> (GEMM1 last round beside early GEMM2 tiles)",
-                 "gemm_tiled<false, false> (rest of GEMM2, reduce folded in)",
-                 "gemm_stream<true>, gemm_stream<false> (experts with <= 32 rows)"]
-                if gather else ["gemm_f32<true>", "gemm_f32<false>"])
     if bf16 and both_flops / both_bytes >= ridge:
         ach = both_flops / t_gemm / 1e12
         roofline = {"bound": "mfma", "achieved": ach, "peak": peak_mm, "unit": "TFLOP/s",
@@ -708,8 +745,10 @@ def main():
                                           "grouped_gemm.hip"),
                 "us_per_step": gemm_fwd_us, "algorithmic_flops": both_flops,
                 "algorithmic_bytes": both_bytes, "launches": launches,
-                "method": "HIP events around moe_forward in eager steps, minus the reduce"
-                          + ("" if gather else " and the expand") + " of the staged steps"}
+                "method": "HIP events around moe_forward in eager steps"
+                          + ("" if reduce_in_gemm2 else ", minus the reduce")
+                          + ("" if gather else " and the expand")
+                          + ("" if reduce_in_gemm2 and gather else " of the staged steps")}
     log(f"[bench] forward GEMM launches {gemm_fwd_us:10.2f} us  {roofline['achieved']:9.1f} "
         f"{roofline['unit']}  {100 * roofline['frac']:5.1f}% of peak (forward {fwd_us:.2f} us)")
     for k, v in stages.items():
@@ -766,7 +805,7 @@ def main():
 
     cold = {}
     y2 = torch.empty_like(y)
-    if gather:
+    if fused:
         cold["combine_reduce"] = cold_us(lambda: tr.combine_reduce_multi(p, w, y2, stream=stream))
         cold["expand_alone"] = cold_us(lambda: tr.expand(p, x, stream=stream))
         # the full reduce over every received row (moe_combine_reduce after the
@@ -777,12 +816,15 @@ def main():
                       "expand_alone": (T_loc + R) * H * b + 4 * T * K,
                       "combine_reduce_full": R * H * b + T * H * b + 8 * T * K}
     else:
+        # fp32 forwards gather x in GEMM1 too: moe_expand is timed alone
+        ek = "expand_alone" if gather else "expand"
         cold["combine_reduce"] = cold_us(lambda: tr.combine_reduce(p, w, y=y, stream=stream))
-        cold["expand"] = cold_us(lambda: tr.expand(p, x, stream=stream))
-        cold_bytes = {"combine_reduce": work["combine_reduce"][1], "expand": work["expand"][1]}
+        cold[ek] = cold_us(lambda: tr.expand(p, x, stream=stream))
+        cold_bytes = {"combine_reduce": work["combine_reduce"][1],
+                      ek: (T_loc + R) * H * b + 4 * T * K}
     # the GEMM stages cold: weight-streaming shapes (arithmetic intensity
     # below the ridge) are claimed against HBM on these numbers
-    if gather:
+    if fused:
         cold["gemm_up"] = cold_us(lambda: tr.grouped_gemm_up_x(p, x, w1, stream=stream))
         cold["gemm_down"] = cold_us(lambda: tr.grouped_gemm_down_y(p, w2, w, y2, stream=stream))
         cold_bytes["gemm_up"] = gemm_bytes["gemm_up"]
