@@ -69,6 +69,9 @@ def parse():
     ap.add_argument("--forward-only", action="store_true",
                     help="only warmup + timed plan + moe_forward steps, as the library runs them "
                          "(for profiler runs of the forward's own launches)")
+    ap.add_argument("--dense-expert-only", action="store_true",
+                    help="time only the tiled GEMM on one dense expert of the config's H and I "
+                         "(8192 rows) beside hipBLASLt on the same operands (for counter runs)")
     ap.add_argument("--lowbatch-only", action="store_true",
                     help="only the low-batch combine and cross-rank epilogue measurements "
                          "(for profiler runs of those launches)")
@@ -421,6 +424,57 @@ def dense_calibration(M: int, H: int, I: int, stream, reps: int = 10):
     return out
 
 
+def dense_expert(M: int, H: int, I: int, stream, reps: int = 10):
+    """The tiled grouped GEMM on one dense expert of M rows (every row routed
+    to expert 0, tiled mode) beside torch.matmul (hipBLASLt) on the same
+    operands: [M, H] x [H, 2I] with SwiGLU, and [M, I] x [I, H]. Separates the
+    kernel's own efficiency from what ragged experts cost it. A calibration,
+    not a target."""
+    import torch
+
+    import top_reduce_amd as tr
+
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(6)
+    x = torch.randn((M, H), generator=g, device=dev).to(torch.bfloat16)
+    w1 = (torch.randn((1, 2 * I, H), generator=g, device=dev) / H ** 0.5).to(torch.bfloat16)
+    w2 = (torch.randn((1, H, I), generator=g, device=dev) / I ** 0.5).to(torch.bfloat16)
+    idx = torch.zeros((M, 1), dtype=torch.int64, device=dev)
+    p = tr.plan(idx, E=1, H=H, I=I, flags=tr.FLAG_GEMM_FORCE_TILED, stream=stream)
+    hcur = p.views()["h"][:M]
+    b1, b2 = w1[0], w2[0]
+    c1 = torch.empty((M, 2 * I), dtype=torch.bfloat16, device=dev)
+    c2 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    runs = (lambda: tr.grouped_gemm_up_x(p, x, w1, stream=stream),
+            lambda: tr.grouped_gemm_down(p, w2, stream=stream),
+            lambda: torch.matmul(x, b1.t(), out=c1),
+            lambda: torch.matmul(hcur, b2.t(), out=c2))
+    for _ in range(2):
+        for r in runs:
+            r()
+    torch.cuda.synchronize()
+    t = [0.0] * 4
+    for _ in range(reps):
+        for i, r in enumerate(runs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            r()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t[i] += e0.elapsed_time(e1) * 1e3 / reps
+    f = (4.0 * M * I * H, 2.0 * M * H * I)
+    frac = [f[i % 2] / (t[i] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS for i in range(4)]
+    out = {"shapes_mnk": [[M, 2 * I, H], [M, H, I]], "unit": "us",
+           "tiled_kernel_us": [t[0], t[1]], "tiled_kernel_frac": [frac[0], frac[1]],
+           "hipblaslt_us": [t[2], t[3]], "hipblaslt_frac": [frac[2], frac[3]],
+           "note": "one dense expert, N(0,1) activations; calibration only"}
+    log(f"[bench] dense expert M={M}: tiled kernel {t[0]:.1f} + {t[1]:.1f} us "
+        f"({frac[0]:.3f}, {frac[1]:.3f} of peak), hipBLASLt {t[2]:.1f} + {t[3]:.1f} us "
+        f"({frac[2]:.3f}, {frac[3]:.3f})")
+    del x, w1, w2, p, c1, c2
+    return out
+
+
 def copy_reference(stream, nbytes: int = 1 << 30, reps: int = 20):
     """Bandwidth of a plain device copy (torch's elementwise negation, read
     nbytes + write nbytes) on the same GPU in the same run: the practical
@@ -468,6 +522,12 @@ def main():
         out = {"lowbatch_combine": lowbatch_combine(args.steps),
                "lowbatch_epilogue": lowbatch_epilogue(args.steps)}
         print(json.dumps({"metric": METRIC, "lowbatch_only": True, **out}), flush=True)
+        return
+    if args.dense_expert_only:
+        spec = gen.CONFIGS[args.config]
+        H, I = spec.H, spec.I
+        out = dense_expert(8192, H, I, torch.cuda.current_stream(dev), reps=args.steps)
+        print(json.dumps({"metric": METRIC, "dense_expert_only": True, "dense_expert": out}), flush=True)
         return
     t0 = time.time()
     wl = gen.make_workload(args.config, T=args.T, with_weights=True)
@@ -774,6 +834,8 @@ def main():
     }
     if bf16 and both_flops / both_bytes >= ridge:
         result["dense_bf16_calibration"] = dense_calibration(R, H, I, stream)
+        if H % 256 == 0 and I % 128 == 0:
+            result["dense_expert"] = dense_expert(8192, H, I, stream)
     if gather:
         result["expand_alone"] = expand_alone()
 
