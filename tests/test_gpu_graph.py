@@ -76,3 +76,33 @@ def test_forward_graph_replay(T, E, H, I):
         torch.cuda.synchronize()
         assert _same(y, y_eager), f"graph replay {rep} differs from the eager forward"
         assert _same(y2, y_eager), f"eager forward after replay {rep} differs"
+
+
+# decode batches: the route scan's single-block kernel, the decode GEMM and
+# GEMM2 with the reduce folded in, replayed with eager decode steps between
+@pytest.mark.parametrize("T", [1, 2])
+def test_decode_graph_replay(T):
+    import gen
+    from tests._gpu import upload
+    say(f"decode graph replay: c3 T={T}")
+    wl = gen.make_workload("c3", T=T, with_weights=True)
+    d = upload(wl)
+    p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I)
+    y_eager = tr.forward(p, d["x"], d["w"], d["w1"], d["w2"])
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_eager)
+    stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        q = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, stream=cap)
+        tr.forward(q, d["x"], d["w"], d["w1"], d["w2"], y=y, stream=cap)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        y.zero_()
+        graph.replay()
+        y2 = tr.forward(tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I), d["x"], d["w"], d["w1"], d["w2"])
+        torch.cuda.synchronize()
+        assert _same(y, y_eager), f"graph replay {rep} differs from the eager forward"
+        assert _same(y2, y_eager), f"eager forward after replay {rep} differs"
