@@ -106,3 +106,69 @@ def test_decode_graph_replay(T):
         torch.cuda.synchronize()
         assert _same(y, y_eager), f"graph replay {rep} differs from the eager forward"
         assert _same(y2, y_eager), f"eager forward after replay {rep} differs"
+
+
+def _replay_matches(capture_step, eager_step, y, reps=4):
+    """Capture capture_step() (writing y) on a side stream, replay it reps
+    times with eager_step() between, each replay bit-equal to the eager
+    output."""
+    y_eager = eager_step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        capture_step(cap)
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        y.zero_()
+        graph.replay()
+        y2 = eager_step()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_eager.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(y2.view(torch.int16), y_eager.view(torch.int16)), f"eager after {rep}"
+
+
+def test_fp32_graph_replay():
+    """The fp32 path (c1): GEMM1 gathering x, fp32 MFMA GEMMs, full reduce."""
+    import gen
+    from tests._gpu import upload
+    say("fp32 graph replay: c1")
+    wl = gen.make_workload("c1", with_weights=True)
+    d = upload(wl)
+    y = torch.empty((wl.T, wl.H), dtype=torch.float32, device="cuda")
+
+    def eager():
+        p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch.float32)
+        return tr.forward(p, d["x"], d["w"], d["w1"], d["w2"])
+
+    def capture(s):
+        q = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, dtype=torch.float32, stream=s)
+        tr.forward(q, d["x"], d["w"], d["w1"], d["w2"], y=y, stream=s)
+
+    _replay_matches(capture, eager, y)
+
+
+def test_padded_plan_graph_replay():
+    """A DP-padded plan (block counts read on the device, padding rows'
+    stale ids never read) and its forward, c4's buffer."""
+    import gen
+    from tests._gpu import upload
+    say("padded plan graph replay: c4")
+    wl = gen.make_workload("c4", with_weights=True)
+    d = upload(wl)
+    bc = torch.tensor(gen.C4_WORKER_COUNTS, dtype=torch.int32, device="cuda")
+    y = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+
+    def eager():
+        p = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, block_rows=gen.C4_WORKER_ROWS,
+                    block_counts=bc)
+        return tr.forward(p, d["x"], d["w"], d["w1"], d["w2"])
+
+    def capture(s):
+        q = tr.plan(d["idx"], E=wl.E, H=wl.H, I=wl.I, block_rows=gen.C4_WORKER_ROWS,
+                    block_counts=bc, stream=s)
+        tr.forward(q, d["x"], d["w"], d["w1"], d["w2"], y=y, stream=s)
+
+    _replay_matches(capture, eager, y)
